@@ -1,0 +1,202 @@
+"""MoonEP hot path on AMD MI355X (gfx950): Python binding of libmoonep.so.
+
+`Buffer` mirrors the MoonEP README's Buffer (MoonshotAI/MoonEP mirror,
+"API guide"), for all R EP ranks of one GPU at once.  Each method is one call
+of the C ABI of the same name (include/moonep.h) with torch tensors supplying
+device memory and the current stream; nothing is computed in Python.
+
+    buf = Buffer(R=8, S=4096, K=8, E=256, B=32, H=7168, Hp=2048, token_padding=128)
+    plan = buf.plan(topk)                           # moonep_plan
+    x_nvs, rw_nvs = buf.dispatch(plan, x, rw)       # moonep_dispatch
+    buf.prefetch_weight(plan, home, pool)           # moonep_prefetch_weight
+    buf.expert_ffn(plan, x_nvs, home, pool, z, y)   # moonep_expert_ffn
+    out, rw_sk = buf.combine(plan, y, rw_nvs)       # moonep_combine
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _abi
+from ._abi import MoonepError, lib  # noqa: F401
+
+__all__ = ["Buffer", "Plan", "MoonepError", "lib"]
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev_ptr(t, dtype, shape, name, nullable=False):
+    if t is None:
+        if nullable:
+            return None
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+class Plan:
+    """Device arrays of one plan (see moonep_plan_t)."""
+
+    def __init__(self, cfg, device):
+        self.arrays = {}
+        self._store = []
+        for i, name in enumerate(_abi.PLAN_ARRAYS):
+            n = _abi.plan_len(cfg, i)
+            # zero-length arrays (B = 0) still get a valid device pointer
+            store = torch.empty(max(n, 1), dtype=torch.int32, device=device)
+            self.arrays[name] = store[:n]
+            self._store.append(store)
+        self.struct = _abi.MoonepPlan(*[s.data_ptr() for s in self._store])
+
+    def __getattr__(self, name):
+        arrays = self.__dict__.get("arrays")
+        if arrays is not None and name in arrays:
+            return arrays[name]
+        raise AttributeError(name)
+
+
+class Buffer:
+    """Handle of the MoonEP path for R ranks on the current device."""
+
+    def __init__(self, R, S, K, E, B=None, H=7168, Hp=2048, token_padding=128, num_cus=0,
+                 device="cuda"):
+        if B is None:
+            B = E // R
+        self.R, self.S, self.K, self.E, self.B = R, S, K, E, B
+        self.H, self.Hp, self.token_padding = H, Hp, token_padding
+        self.device = torch.device(device)
+        self.cfg = _abi.config(R, S, K, E, B, H, Hp, token_padding, num_cus)
+        self.NvS = _abi.nvs(self.cfg)
+        if self.NvS < 0:
+            raise MoonepError(_abi.MOONEP_ERR_CONFIG, "Buffer")
+        self._h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _abi.check(lib().moonep_create(ctypes.byref(self.cfg), ctypes.byref(self._h)),
+                       "moonep_create")
+
+    # -- lifecycle -----------------------------------------------------------
+    def destroy(self):
+        if self._h:
+            _abi.check(lib().moonep_destroy(self._h), "moonep_destroy")
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+    def new_plan(self):
+        return Plan(self.cfg, self.device)
+
+    # -- calls -----------------------------------------------------------------
+    def plan(self, topk, tokens_per_expert=None, plan=None):
+        plan = plan or self.new_plan()
+        R, S, K, E = self.R, self.S, self.K, self.E
+        p_topk = _dev_ptr(topk, torch.int32, (R, S, K), "topk")
+        p_tpe = _dev_ptr(tokens_per_expert, torch.int32, (R, E), "tokens_per_expert", True)
+        _abi.check(lib().moonep_plan(self._h, p_topk, p_tpe, ctypes.byref(plan.struct), _stream()),
+                   "moonep_plan")
+        return plan
+
+    def dispatch(self, plan, x, rw=None, x_nvs=None, rw_nvs=None):
+        R, S, K, NvS = self.R, self.S, self.K, self.NvS
+        W = x.shape[-1]
+        if x_nvs is None:
+            x_nvs = torch.empty((R, NvS, W), dtype=torch.bfloat16, device=x.device)
+        if rw is not None and rw_nvs is None:
+            rw_nvs = torch.empty((R, NvS), dtype=torch.float32, device=x.device)
+        args = (_dev_ptr(x, torch.bfloat16, (R, S, W), "x"), int(W),
+                _dev_ptr(rw, torch.float32, (R, S, K), "rw", True),
+                _dev_ptr(x_nvs, torch.bfloat16, (R, NvS, W), "x_nvs"),
+                _dev_ptr(rw_nvs, torch.float32, (R, NvS), "rw_nvs", True))
+        _abi.check(lib().moonep_dispatch(self._h, ctypes.byref(plan.struct), *args, _stream()),
+                   "moonep_dispatch")
+        return x_nvs, rw_nvs
+
+    def combine(self, plan, y_nvs, rw_nvs=None, out=None, rw_sk=None, gather_rw=True):
+        R, S, K, NvS = self.R, self.S, self.K, self.NvS
+        W = y_nvs.shape[-1]
+        if out is None:
+            out = torch.empty((R, S, W), dtype=torch.bfloat16, device=y_nvs.device)
+        if rw_nvs is not None and rw_sk is None and gather_rw:
+            rw_sk = torch.empty((R, S, K), dtype=torch.float32, device=y_nvs.device)
+        args = (_dev_ptr(y_nvs, torch.bfloat16, (R, NvS, W), "y_nvs"), int(W),
+                _dev_ptr(rw_nvs, torch.float32, (R, NvS), "rw_nvs", True),
+                _dev_ptr(out, torch.bfloat16, (R, S, W), "out"),
+                _dev_ptr(rw_sk, torch.float32, (R, S, K), "rw_sk", True))
+        _abi.check(lib().moonep_combine(self._h, ctypes.byref(plan.struct), *args, _stream()),
+                   "moonep_combine")
+        return out, rw_sk
+
+    def _weights(self, ts, pool):
+        R, E, B, H, Hp = self.R, self.E, self.B, self.H, self.Hp
+        if len(ts) != 3:
+            raise ValueError("three projections (gate, up, down) expected")
+        shape = (R, B, H, Hp) if pool else (E, H, Hp)
+        for i, t in enumerate(ts):
+            if pool and B == 0 and t is None:
+                continue
+            _dev_ptr(t, torch.bfloat16, shape, f"{'pool' if pool else 'home'}[{i}]")
+        return _abi.ptr3(ts)
+
+    def prefetch_weight(self, plan, home, pool):
+        _abi.check(lib().moonep_prefetch_weight(self._h, ctypes.byref(plan.struct),
+                                                self._weights(home, False),
+                                                self._weights(pool, True), _stream()),
+                   "moonep_prefetch_weight")
+
+    def expert_ffn(self, plan, x_nvs, home, pool, z_ws=None, y_nvs=None, rank=-1):
+        R, NvS, H, Hp = self.R, self.NvS, self.H, self.Hp
+        if z_ws is None:
+            z_ws = torch.empty((R, NvS, Hp), dtype=torch.bfloat16, device=x_nvs.device)
+        if y_nvs is None:
+            y_nvs = torch.empty((R, NvS, H), dtype=torch.bfloat16, device=x_nvs.device)
+        args = (int(rank), _dev_ptr(x_nvs, torch.bfloat16, (R, NvS, H), "x_nvs"),
+                self._weights(home, False), self._weights(pool, True),
+                _dev_ptr(z_ws, torch.bfloat16, (R, NvS, Hp), "z_ws"),
+                _dev_ptr(y_nvs, torch.bfloat16, (R, NvS, H), "y_nvs"))
+        _abi.check(lib().moonep_expert_ffn(self._h, ctypes.byref(plan.struct), *args, _stream()),
+                   "moonep_expert_ffn")
+        return z_ws, y_nvs
+
+    def expert_wgrad(self, plan, a_nvs, b_nvs, grad_home, reduce_buf, rank=-1):
+        R, NvS, E, B, H, Hp = self.R, self.NvS, self.E, self.B, self.H, self.Hp
+        args = (int(rank), _dev_ptr(a_nvs, torch.bfloat16, (R, NvS, H), "a_nvs"),
+                _dev_ptr(b_nvs, torch.bfloat16, (R, NvS, Hp), "b_nvs"),
+                _dev_ptr(grad_home, torch.float32, (E, H, Hp), "grad_home"),
+                _dev_ptr(reduce_buf, torch.float32, (R, B, H, Hp), "reduce_buf"))
+        _abi.check(lib().moonep_expert_wgrad(self._h, ctypes.byref(plan.struct), *args, _stream()),
+                   "moonep_expert_wgrad")
+
+    def reduce_grad(self, plan, grad_home, reduce_buf):
+        R, E, B, H, Hp = self.R, self.E, self.B, self.H, self.Hp
+        for i in range(3):
+            _dev_ptr(grad_home[i], torch.float32, (E, H, Hp), f"grad_home[{i}]")
+            _dev_ptr(reduce_buf[i], torch.float32, (R, B, H, Hp), f"reduce_buf[{i}]")
+        _abi.check(lib().moonep_reduce_grad(self._h, ctypes.byref(plan.struct),
+                                            _abi.ptr3(grad_home), _abi.ptr3(reduce_buf),
+                                            _stream()),
+                   "moonep_reduce_grad")
+
+    def read_stats(self, plan):
+        import numpy as np
+        out = np.zeros(_abi.STAT_FIXED + 2 * self.R, dtype=np.int32)
+        _abi.check(lib().moonep_read_stats(self._h, ctypes.byref(plan.struct),
+                                           out.ctypes.data_as(ctypes.c_void_p), _stream()),
+                   "moonep_read_stats")
+        return out
+
+
+# fail at import time, loudly, when the native library is missing
+lib()

@@ -1,0 +1,103 @@
+"""ctypes binding of libmoonep.so (the C ABI declared in include/moonep.h).
+
+Argument marshalling only: torch tensors provide device memory and the
+current HIP stream; shapes, dtypes, devices and contiguity are checked here
+because the C ABI receives bare pointers.  Every computation happens in the
+library's gfx950 kernels; if the library cannot be loaded, importing fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoonep.so")
+
+MOONEP_OK, MOONEP_ERR_ARG, MOONEP_ERR_CONFIG, MOONEP_ERR_MODE, MOONEP_ERR_HIP, MOONEP_ERR_NOMEM = range(6)
+STAT_ERROR, STAT_DUPS, STAT_MAX_LOAD, STAT_DONATIONS, STAT_PAD_ROWS, STAT_MAXVIO = range(6)
+STAT_FIXED = 8
+PLAN_ARRAYS = ["counts", "dest", "src", "cu_seqlens", "seg_tokens", "prefetch_src", "stats", "aux"]
+
+
+class MoonepConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("R", "S", "K", "E", "B", "H", "Hp", "token_padding", "num_cus")]
+
+
+class MoonepPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in PLAN_ARRAYS]
+
+
+class MoonepError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoonep.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m grouped_gemm_moonep_amd.build`")
+    try:
+        import torch  # noqa: F401  (share torch's HIP runtime if it is loaded)
+    except ImportError:
+        pass
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    P3 = ctypes.c_void_p * 3
+    sig = {
+        "moonep_abi_version": (i32, []),
+        "moonep_status_string": (ctypes.c_char_p, [i32]),
+        "moonep_nvs": (i64, [ctypes.POINTER(MoonepConfig)]),
+        "moonep_plan_len": (i64, [ctypes.POINTER(MoonepConfig), i32]),
+        "moonep_create": (i32, [ctypes.POINTER(MoonepConfig), ctypes.POINTER(vp)]),
+        "moonep_destroy": (i32, [vp]),
+        "moonep_plan": (i32, [vp, vp, vp, ctypes.POINTER(MoonepPlan), vp]),
+        "moonep_dispatch": (i32, [vp, ctypes.POINTER(MoonepPlan), vp, i32, vp, vp, vp, vp]),
+        "moonep_combine": (i32, [vp, ctypes.POINTER(MoonepPlan), vp, i32, vp, vp, vp, vp]),
+        "moonep_prefetch_weight": (i32, [vp, ctypes.POINTER(MoonepPlan), P3, P3, vp]),
+        "moonep_expert_ffn": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, P3, P3, vp, vp, vp]),
+        "moonep_expert_wgrad": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, vp, vp, vp, vp]),
+        "moonep_reduce_grad": (i32, [vp, ctypes.POINTER(MoonepPlan), P3, P3, vp]),
+        "moonep_read_stats": (i32, [vp, ctypes.POINTER(MoonepPlan), vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    if L.moonep_abi_version() != 1:
+        raise ImportError("libmoonep.so ABI version mismatch")
+    _lib = L
+    return L
+
+
+def status_string(s):
+    return lib().moonep_status_string(int(s)).decode()
+
+
+def check(status, where):
+    if status != MOONEP_OK:
+        raise MoonepError(status, where)
+
+
+def config(R, S, K, E, B, H, Hp, token_padding, num_cus=0):
+    return MoonepConfig(R, S, K, E, B, H, Hp, token_padding, num_cus)
+
+
+def nvs(cfg: MoonepConfig) -> int:
+    return int(lib().moonep_nvs(ctypes.byref(cfg)))
+
+
+def plan_len(cfg: MoonepConfig, which: int) -> int:
+    return int(lib().moonep_plan_len(ctypes.byref(cfg), which))
+
+
+def ptr3(ts):
+    return (ctypes.c_void_p * 3)(*[None if t is None else t.data_ptr() for t in ts])

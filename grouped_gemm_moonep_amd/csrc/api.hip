@@ -1,0 +1,261 @@
+// Host side of the C ABI: configuration checks, handle scratch, argument
+// validation, and the launches.  Nothing here runs on the CPU instead of the
+// GPU: every step of the path is a kernel.
+#include <stdlib.h>
+#include <string.h>
+
+#include "internal.h"
+
+namespace moonep {
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool dims_from_config(const moonep_config_t* cfg, Dims* out) {
+  if (!cfg) return false;
+  const moonep_config_t& c = *cfg;
+  if (c.R < 1 || c.R > kMaxR) return false;
+  if (c.E < c.R || c.E % c.R || c.E > 1024) return false;
+  if ((int64_t)c.R * c.E > kMaxRE) return false;
+  if (c.K < 1 || c.K > c.E || c.K > kMaxK) return false;
+  if (c.S < 1) return false;
+  if ((int64_t)c.R * c.S * c.K >= (int64_t(1) << 31)) return false;
+  const int L = c.E / c.R;
+  if (c.B < 0 || c.B > L) return false;
+  if ((int64_t)c.R * (c.E + c.B) > kMaxRE) return false;
+  if (c.token_padding < 1) return false;
+  if (c.H < 64 || c.H % 64 || c.Hp < 64 || c.Hp % 64) return false;
+  if (c.num_cus < 0) return false;
+  const int64_t nvs = (int64_t)c.S * c.K + 2LL * L * c.token_padding;
+  if ((int64_t)c.R * nvs >= (int64_t(1) << 31)) return false;
+  const int64_t wmax = c.H > c.Hp ? c.H : c.Hp;
+  if ((int64_t)c.R * nvs * wmax >= (int64_t(1) << 40)) return false;
+  Dims d;
+  d.R = c.R; d.S = c.S; d.K = c.K; d.E = c.E; d.B = c.B; d.H = c.H;
+  d.Hp = c.Hp; d.tp = c.token_padding; d.num_cus = c.num_cus;
+  d.L = L;
+  d.NvS = nvs;
+  d.nch = (int)ceil_div(c.S, kPlanChunk);
+  const int64_t RB = (int64_t)c.R * c.B;
+  AuxLayout& a = d.aux;
+  a.act = 0;
+  a.pf_n = a.act + 2LL * c.E;
+  a.pf = a.pf_n + 1;
+  a.dup_n = a.pf + RB;
+  a.dup_e = a.dup_n + 1;
+  a.dup_first = a.dup_e + RB;
+  a.dup_cnt = a.dup_first + RB;
+  a.hold = a.dup_cnt + RB;
+  a.total = a.hold + RB;
+  *out = d;
+  return true;
+}
+
+}  // namespace moonep
+
+using namespace moonep;
+
+struct moonep_ctx {
+  Ctx c;
+};
+
+static bool aligned(const void* p, size_t a) {
+  return ((uintptr_t)p % a) == 0;
+}
+
+static moonep_status_t hip_status(hipError_t e) {
+  return e == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
+}
+
+static bool plan_ok(const moonep_plan_t* p) {
+  if (!p) return false;
+  const int32_t* a[] = {p->counts, p->dest, p->src, p->cu_seqlens,
+                        p->seg_tokens, p->prefetch_src, p->stats, p->aux};
+  for (const int32_t* q : a)
+    if (!q || !aligned(q, 4)) return false;
+  return true;
+}
+
+extern "C" {
+
+int32_t moonep_abi_version(void) { return MOONEP_ABI_VERSION; }
+
+const char* moonep_status_string(moonep_status_t s) {
+  switch (s) {
+    case MOONEP_OK: return "ok";
+    case MOONEP_ERR_ARG: return "invalid argument (null/misaligned pointer, width or rank)";
+    case MOONEP_ERR_CONFIG: return "configuration outside the supported range";
+    case MOONEP_ERR_MODE: return "training call needs B == E/R";
+    case MOONEP_ERR_HIP: return "HIP runtime error";
+    case MOONEP_ERR_NOMEM: return "device allocation failed";
+    default: return "unknown status";
+  }
+}
+
+int64_t moonep_nvs(const moonep_config_t* cfg) {
+  Dims d;
+  return dims_from_config(cfg, &d) ? d.NvS : -1;
+}
+
+int64_t moonep_plan_len(const moonep_config_t* cfg, int32_t which) {
+  Dims d;
+  if (!dims_from_config(cfg, &d)) return -1;
+  switch (which) {
+    case MOONEP_PLAN_COUNTS: return (int64_t)d.R * d.E;
+    case MOONEP_PLAN_DEST: return (int64_t)d.R * d.S * d.K;
+    case MOONEP_PLAN_SRC: return (int64_t)d.R * d.NvS;
+    case MOONEP_PLAN_CU_SEQLENS: return (int64_t)d.R * (d.E + d.B);
+    case MOONEP_PLAN_SEG_TOKENS: return (int64_t)d.R * (d.E + d.B);
+    case MOONEP_PLAN_PREFETCH_SRC: return (int64_t)d.R * d.B;
+    case MOONEP_PLAN_STATS: return MOONEP_STAT_FIXED + 2LL * d.R;
+    case MOONEP_PLAN_AUX: return d.aux.total;
+    default: return -1;
+  }
+}
+
+moonep_status_t moonep_create(const moonep_config_t* cfg, moonep_handle_t* out) {
+  if (!out) return MOONEP_ERR_ARG;
+  Dims d;
+  if (!dims_from_config(cfg, &d)) return MOONEP_ERR_CONFIG;
+  moonep_ctx* h = (moonep_ctx*)calloc(1, sizeof(moonep_ctx));
+  if (!h) return MOONEP_ERR_NOMEM;
+  Ctx& c = h->c;
+  c.d = d;
+  if (hipGetDevice(&c.device) != hipSuccess ||
+      hipDeviceGetAttribute(&c.num_cu_device, hipDeviceAttributeMultiprocessorCount,
+                            c.device) != hipSuccess) {
+    free(h);
+    return MOONEP_ERR_HIP;
+  }
+  c.max_tiles = (int)(ceil_div(d.NvS, kGemmTileM) + 2 * d.L);
+  struct { int32_t** p; int64_t n; } allocs[] = {
+      {&c.cc, (int64_t)d.R * d.nch * d.E},
+      {&c.rankpre, (int64_t)d.R * d.E},
+      {&c.shift, (int64_t)d.R * d.E},
+      {&c.pieces, (int64_t)d.R * (d.R + 1) * 2},
+      {&c.npieces, d.R},
+      {&c.line, d.E},
+      {&c.chunk_err, (int64_t)d.R * d.nch},
+      {&c.tiles, (int64_t)d.R * c.max_tiles * 4},
+      {&c.ntiles, d.R},
+  };
+  for (auto& a : allocs) {
+    if (hipMalloc((void**)a.p, (size_t)a.n * sizeof(int32_t)) != hipSuccess) {
+      moonep_destroy(h);
+      return MOONEP_ERR_NOMEM;
+    }
+  }
+  *out = h;
+  return MOONEP_OK;
+}
+
+moonep_status_t moonep_destroy(moonep_handle_t h) {
+  if (!h) return MOONEP_OK;
+  Ctx& c = h->c;
+  int32_t* ptrs[] = {c.cc, c.rankpre, c.shift, c.pieces, c.npieces, c.line,
+                     c.chunk_err, c.tiles, c.ntiles};
+  hipError_t err = hipSuccess;
+  for (int32_t* p : ptrs)
+    if (p) {
+      hipError_t e = hipFree(p);
+      if (e != hipSuccess) err = e;
+    }
+  free(h);
+  return hip_status(err);
+}
+
+moonep_status_t moonep_plan(moonep_handle_t h, const int32_t* topk,
+                            const int32_t* tokens_per_expert,
+                            const moonep_plan_t* plan, hipStream_t stream) {
+  if (!h || !topk || !aligned(topk, 4) || !plan_ok(plan)) return MOONEP_ERR_ARG;
+  if (tokens_per_expert && !aligned(tokens_per_expert, 4)) return MOONEP_ERR_ARG;
+  return hip_status(launch_plan(h->c, topk, tokens_per_expert, *plan, stream));
+}
+
+moonep_status_t moonep_dispatch(moonep_handle_t h, const moonep_plan_t* plan,
+                                const uint16_t* x, int32_t W, const float* rw,
+                                uint16_t* x_nvs, float* rw_nvs,
+                                hipStream_t stream) {
+  if (!h || !plan_ok(plan) || !x || !x_nvs) return MOONEP_ERR_ARG;
+  if (W <= 0 || W % 8 || !aligned(x, 16) || !aligned(x_nvs, 16)) return MOONEP_ERR_ARG;
+  if ((rw == nullptr) != (rw_nvs == nullptr)) return MOONEP_ERR_ARG;
+  if (rw && (!aligned(rw, 4) || !aligned(rw_nvs, 4))) return MOONEP_ERR_ARG;
+  return hip_status(launch_dispatch(h->c, *plan, x, W, rw, x_nvs, rw_nvs, stream));
+}
+
+moonep_status_t moonep_combine(moonep_handle_t h, const moonep_plan_t* plan,
+                               const uint16_t* y_nvs, int32_t W,
+                               const float* rw_nvs, uint16_t* out,
+                               float* rw_sk, hipStream_t stream) {
+  if (!h || !plan_ok(plan) || !y_nvs || !out) return MOONEP_ERR_ARG;
+  if (W <= 0 || W % 8 || !aligned(y_nvs, 16) || !aligned(out, 16)) return MOONEP_ERR_ARG;
+  if (rw_sk && !rw_nvs) return MOONEP_ERR_ARG;
+  if ((rw_nvs && !aligned(rw_nvs, 4)) || (rw_sk && !aligned(rw_sk, 4))) return MOONEP_ERR_ARG;
+  return hip_status(launch_combine(h->c, *plan, y_nvs, W, rw_nvs, out, rw_sk, stream));
+}
+
+moonep_status_t moonep_prefetch_weight(moonep_handle_t h, const moonep_plan_t* plan,
+                                       const uint16_t* const home[3],
+                                       uint16_t* const pool[3], hipStream_t stream) {
+  if (!h || !plan_ok(plan) || !home || !pool) return MOONEP_ERR_ARG;
+  for (int p = 0; p < 3; ++p) {
+    if (!home[p] || !aligned(home[p], 16)) return MOONEP_ERR_ARG;
+    if (h->c.d.B > 0 && (!pool[p] || !aligned(pool[p], 16))) return MOONEP_ERR_ARG;
+  }
+  if (h->c.d.B == 0) return MOONEP_OK;
+  return hip_status(launch_prefetch(h->c, *plan, home, pool, stream));
+}
+
+moonep_status_t moonep_expert_ffn(moonep_handle_t h, const moonep_plan_t* plan,
+                                  int32_t rank, const uint16_t* x_nvs,
+                                  const uint16_t* const home[3],
+                                  const uint16_t* const pool[3], uint16_t* z_ws,
+                                  uint16_t* y_nvs, hipStream_t stream) {
+  if (!h || !plan_ok(plan) || !x_nvs || !z_ws || !y_nvs || !home || !pool)
+    return MOONEP_ERR_ARG;
+  if (rank < -1 || rank >= h->c.d.R) return MOONEP_ERR_ARG;
+  if (!aligned(x_nvs, 16) || !aligned(z_ws, 16) || !aligned(y_nvs, 16)) return MOONEP_ERR_ARG;
+  if ((void*)z_ws == (void*)x_nvs || (void*)z_ws == (void*)y_nvs) return MOONEP_ERR_ARG;
+  for (int p = 0; p < 3; ++p) {
+    if (!home[p] || !aligned(home[p], 16)) return MOONEP_ERR_ARG;
+    if (h->c.d.B > 0 && (!pool[p] || !aligned(pool[p], 16))) return MOONEP_ERR_ARG;
+  }
+  return hip_status(launch_ffn(h->c, *plan, rank, x_nvs, home, pool, z_ws, y_nvs, stream));
+}
+
+moonep_status_t moonep_expert_wgrad(moonep_handle_t h, const moonep_plan_t* plan,
+                                    int32_t rank, const uint16_t* a_nvs,
+                                    const uint16_t* b_nvs, float* grad_home,
+                                    float* reduce_buf, hipStream_t stream) {
+  if (!h || !plan_ok(plan) || !a_nvs || !b_nvs || !grad_home) return MOONEP_ERR_ARG;
+  if (rank < -1 || rank >= h->c.d.R) return MOONEP_ERR_ARG;
+  if (h->c.d.B != h->c.d.L) return MOONEP_ERR_MODE;
+  if (!reduce_buf) return MOONEP_ERR_ARG;
+  if (!aligned(a_nvs, 16) || !aligned(b_nvs, 16) || !aligned(grad_home, 16) ||
+      !aligned(reduce_buf, 16))
+    return MOONEP_ERR_ARG;
+  return hip_status(launch_wgrad(h->c, *plan, rank, a_nvs, b_nvs, grad_home, reduce_buf, stream));
+}
+
+moonep_status_t moonep_reduce_grad(moonep_handle_t h, const moonep_plan_t* plan,
+                                   float* const grad_home[3], float* const reduce_buf[3],
+                                   hipStream_t stream) {
+  if (!h || !plan_ok(plan) || !grad_home || !reduce_buf) return MOONEP_ERR_ARG;
+  if (h->c.d.B != h->c.d.L) return MOONEP_ERR_MODE;
+  for (int p = 0; p < 3; ++p)
+    if (!grad_home[p] || !reduce_buf[p] || !aligned(grad_home[p], 16) ||
+        !aligned(reduce_buf[p], 16))
+      return MOONEP_ERR_ARG;
+  return hip_status(launch_reduce_grad(h->c, *plan, grad_home, reduce_buf, stream));
+}
+
+moonep_status_t moonep_read_stats(moonep_handle_t h, const moonep_plan_t* plan,
+                                  int32_t* host_stats, hipStream_t stream) {
+  if (!h || !plan_ok(plan) || !host_stats) return MOONEP_ERR_ARG;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return MOONEP_ERR_HIP;
+  e = hipMemcpy(host_stats, plan->stats,
+                sizeof(int32_t) * (MOONEP_STAT_FIXED + 2 * h->c.d.R), hipMemcpyDeviceToHost);
+  return hip_status(e);
+}
+
+}  // extern "C"

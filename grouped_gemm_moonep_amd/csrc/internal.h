@@ -1,0 +1,86 @@
+// Internal declarations shared by the host API and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moonep.h"
+
+namespace moonep {
+
+// Tokens handled by one workgroup of the planning kernels (4 waves of 64).
+constexpr int kPlanChunk = 256;
+constexpr int kMaxR = 64;
+constexpr int kMaxRE = 16384;
+constexpr int kMaxK = 32;
+constexpr int kMaxE = 1024;
+
+// Offsets (int32 elements) of the derived tables inside plan.aux.
+struct AuxLayout {
+  int64_t act;      // [R][2L] active rows of each rank, ascending, -1 padded
+  int64_t pf_n;     // [1] used prefetch slots
+  int64_t pf;       // [R*B] used slots d*B+j in ascending (d, j)
+  int64_t dup_n;    // [1] home experts that have prefetch copies
+  int64_t dup_e;    // [R*B] such experts, ascending
+  int64_t dup_first;// [R*B] first holder of each
+  int64_t dup_cnt;  // [R*B] holder count of each
+  int64_t hold;     // [R*B] holder slots d*B+j grouped by expert, ascending d
+  int64_t total;
+};
+
+struct Dims {
+  int R, S, K, E, B, H, Hp, tp, num_cus;
+  int L;          // E / R
+  int64_t NvS;    // slots per rank
+  int nch;        // planning chunks per rank
+  AuxLayout aux;
+};
+
+struct Ctx {
+  Dims d;
+  int device;
+  int num_cu_device;
+  // planning scratch (device)
+  int32_t* cc;        // [R][nch][E] chunk counts, then line-position bases
+  int32_t* rankpre;   // [R][E] sum of counts of lower ranks
+  int32_t* shift;     // [R][E] slot - line position for (d, e)
+  int32_t* pieces;    // [R groups][R+1][2] (hi, rank) of each line piece
+  int32_t* npieces;   // [R]
+  int32_t* line;      // [E] line start a_e
+  int32_t* chunk_err; // [R][nch] routing error bits found per chunk
+  // grouped GEMM schedule scratch (device)
+  int32_t* tiles;     // [R][max_tiles][4] (row, first slot, end slot, 0)
+  int32_t* ntiles;    // [R]
+  int max_tiles;      // per rank, for the FFN / wgrad M-tile size
+};
+
+bool dims_from_config(const moonep_config_t* cfg, Dims* out);
+
+// Kernel launchers (each returns hipGetLastError() after its launches).
+hipError_t launch_plan(const Ctx& c, const int32_t* topk, const int32_t* tpe,
+                       const moonep_plan_t& p, hipStream_t s);
+hipError_t launch_dispatch(const Ctx& c, const moonep_plan_t& p,
+                           const uint16_t* x, int W, const float* rw,
+                           uint16_t* x_nvs, float* rw_nvs, hipStream_t s);
+hipError_t launch_combine(const Ctx& c, const moonep_plan_t& p,
+                          const uint16_t* y, int W, const float* rw_nvs,
+                          uint16_t* out, float* rw_sk, hipStream_t s);
+hipError_t launch_prefetch(const Ctx& c, const moonep_plan_t& p,
+                           const uint16_t* const home[3],
+                           uint16_t* const pool[3], hipStream_t s);
+hipError_t launch_reduce_grad(const Ctx& c, const moonep_plan_t& p,
+                              float* const gh[3], float* const rb[3],
+                              hipStream_t s);
+hipError_t launch_ffn(const Ctx& c, const moonep_plan_t& p, int rank,
+                      const uint16_t* x_nvs, const uint16_t* const home[3],
+                      const uint16_t* const pool[3], uint16_t* z,
+                      uint16_t* y, hipStream_t s);
+hipError_t launch_wgrad(const Ctx& c, const moonep_plan_t& p, int rank,
+                        const uint16_t* a, const uint16_t* b, float* gh,
+                        float* rb, hipStream_t s);
+
+// M-tile of the grouped GEMMs (rows of one segment handled by a workgroup).
+constexpr int kGemmTileM = 256;
+constexpr int kWgradTileM = 64;   // tokens per k-step of the weight gradient
+
+}  // namespace moonep

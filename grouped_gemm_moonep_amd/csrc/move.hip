@@ -1,0 +1,331 @@
+// HBM-bound kernels of the MoonEP path on gfx950: dispatch (fused permute),
+// combine (fused unpermute), prefetch_weight and reduce_grad.
+//
+// MoonEP README (MoonshotAI/MoonEP mirror), "API guide": dispatch writes
+// each token straight into its expert-grouped slot of the destination rank
+// (no separate permute pass), combine brings the K copies of a token back to
+// token-major order, prefetch_weight fills the prefetch rows of the
+// [E+B,H,H'] weight tensor, reduce_grad adds the prefetch-slot gradients of
+// every rank into the owning home rows and zeroes the slots ("Gradient
+// buffer").
+//
+// Design for CDNA4: one wave per token row, 16-byte vector loads and stores
+// (64 lanes x 16 B = 1 KiB per instruction, fully coalesced), all loads of
+// a row chunk in flight before the stores, streaming (non-temporal) access
+// for data that is touched once.  Dispatch reads each token row once and
+// writes it K times (scatter); combine gathers K rows and writes one.  The
+// combine sum uses explicit round-to-nearest fp32 multiply and add
+// (__fmul_rn / __fadd_rn) in ascending k, so it is bit-reproducible.
+#include "internal.h"
+
+namespace moonep {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kUnroll = 8;          // 16-byte vectors per lane in flight
+
+__device__ __forceinline__ int round_up(int n, int m) { return (n + m - 1) / m * m; }
+
+__device__ __forceinline__ float bf16_lo(unsigned v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ unsigned bf16_rne(float f) {
+  const unsigned u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+struct DispatchArgs {
+  const u32x4* x;        // [R*S][W/8]
+  const float* rw;       // [R*S][K] or null
+  u32x4* x_nvs;          // [R*NvS][W/8]
+  float* rw_nvs;         // [R*NvS] or null
+  const int32_t* dest;   // [R*S][K]
+  const int32_t* cu;     // [R][E+B]
+  const int32_t* segn;   // [R][E+B]
+  const int32_t* act;    // [R][2L]
+  int ntok, K, nv, EB, L2, tp, pad_parts, npad_blocks, NvS;
+};
+
+// Blocks [0, npad_blocks): zero the padding rows of one active row (one part
+// of it).  Blocks past that: grid-stride over tokens, one wave per token.
+__global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  if ((int)blockIdx.x < a.npad_blocks) {
+    const int part = blockIdx.x % a.pad_parts;
+    const int dq = blockIdx.x / a.pad_parts;        // d * 2L + q
+    const int row = a.act[dq];
+    if (row < 0) return;
+    const int d = dq / a.L2;
+    const int end = a.cu[d * a.EB + row];
+    const int n = a.segn[d * a.EB + row];
+    const int len = round_up(n, a.tp);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int i = end - len + n + part * kWaves + wv; i < end; i += a.pad_parts * kWaves) {
+      const int64_t slot = (int64_t)d * a.NvS + i;
+      u32x4* dst = a.x_nvs + slot * a.nv;
+      for (int v = lane; v < a.nv; v += 64) __builtin_nontemporal_store(zero, dst + v);
+      if (a.rw_nvs && lane == 0) a.rw_nvs[slot] = 0.0f;
+    }
+    return;
+  }
+  const int nblk = gridDim.x - a.npad_blocks;
+  for (int t = ((int)blockIdx.x - a.npad_blocks) * kWaves + wv; t < a.ntok;
+       t += nblk * kWaves) {
+    const int tok = uniform(t);
+    const u32x4* src = a.x + (int64_t)tok * a.nv;
+    const int32_t* dk = a.dest + (int64_t)tok * a.K;
+    for (int base = 0; base < a.nv; base += 64 * kUnroll) {
+      u32x4 buf[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int v = base + u * 64 + lane;
+        if (v < a.nv) buf[u] = __builtin_nontemporal_load(src + v);
+      }
+      for (int k = 0; k < a.K; ++k) {
+        u32x4* dst = a.x_nvs + (int64_t)uniform(dk[k]) * a.nv;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int v = base + u * 64 + lane;
+          if (v < a.nv) __builtin_nontemporal_store(buf[u], dst + v);
+        }
+      }
+    }
+    if (a.rw && lane < a.K) a.rw_nvs[dk[lane]] = a.rw[(int64_t)tok * a.K + lane];
+  }
+}
+
+struct CombineArgs {
+  const u32x4* y;        // [R*NvS][W/8]
+  const float* rw_nvs;   // [R*NvS] or null
+  u32x4* out;            // [R*S][W/8]
+  float* rw_sk;          // [R*S][K] or null
+  const int32_t* dest;   // [R*S][K]
+  int ntok, K, nv;
+};
+
+constexpr int kCombineUnroll = 2;
+
+template <bool kWeighted>
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  for (int t = (int)blockIdx.x * kWaves + wv; t < a.ntok; t += gridDim.x * kWaves) {
+    const int tok = uniform(t);
+    const int32_t* dk = a.dest + (int64_t)tok * a.K;
+    u32x4* dst = a.out + (int64_t)tok * a.nv;
+    for (int base = 0; base < a.nv; base += 64 * kCombineUnroll) {
+      float acc[kCombineUnroll][8];
+      for (int k = 0; k < a.K; ++k) {
+        const int slot = uniform(dk[k]);
+        const u32x4* src = a.y + (int64_t)slot * a.nv;
+        float wk = 1.0f;
+        if (kWeighted) wk = a.rw_nvs[slot];
+        u32x4 yv[kCombineUnroll];
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+          const int v = base + u * 64 + lane;
+          yv[u] = v < a.nv ? __builtin_nontemporal_load(src + v) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+          float p[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[2 * j] = bf16_lo(yv[u][j]);
+            p[2 * j + 1] = bf16_hi(yv[u][j]);
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float pj = kWeighted ? __fmul_rn(wk, p[j]) : p[j];
+            acc[u][j] = (k == 0) ? pj : __fadd_rn(acc[u][j], pj);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kCombineUnroll; ++u) {
+        const int v = base + u * 64 + lane;
+        if (v < a.nv) {
+          u32x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            o[j] = bf16_rne(acc[u][2 * j]) | (bf16_rne(acc[u][2 * j + 1]) << 16);
+          __builtin_nontemporal_store(o, dst + v);
+        }
+      }
+    }
+    if (kWeighted && a.rw_sk && lane < a.K)
+      a.rw_sk[(int64_t)tok * a.K + lane] = a.rw_nvs[dk[lane]];
+  }
+}
+
+// prefetch: work item = (used slot, projection, chunk of a row).
+struct PrefetchArgs {
+  const u32x4* home[3];  // [E][row_vecs]
+  u32x4* pool[3];        // [R*B][row_vecs]
+  const int32_t* pf;     // [R*B] prefetch_src
+  const int32_t* aux_pf; // used slot list
+  const int32_t* aux_pf_n;
+  int64_t row_vecs;
+  int chunk_vecs, nchunks;
+};
+
+__global__ __launch_bounds__(kThreads) void prefetch_kernel(PrefetchArgs a) {
+  const int n = *a.aux_pf_n;
+  const int64_t items = (int64_t)n * 3 * a.nchunks;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int chunk = (int)(it % a.nchunks);
+    const int proj = (int)((it / a.nchunks) % 3);
+    const int q = (int)(it / ((int64_t)a.nchunks * 3));
+    const int slot = a.aux_pf[q];
+    const int e = a.pf[slot];
+    const u32x4* src = a.home[proj] + (int64_t)e * a.row_vecs;
+    u32x4* dst = a.pool[proj] + (int64_t)slot * a.row_vecs;
+    const int64_t v0 = (int64_t)chunk * a.chunk_vecs;
+    int64_t v1 = v0 + a.chunk_vecs;
+    if (v1 > a.row_vecs) v1 = a.row_vecs;
+    for (int64_t v = v0 + threadIdx.x; v < v1; v += kThreads * 4) {
+      u32x4 b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (v + u * kThreads < v1) b[u] = __builtin_nontemporal_load(src + v + u * kThreads);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (v + u * kThreads < v1) __builtin_nontemporal_store(b[u], dst + v + u * kThreads);
+    }
+  }
+}
+
+// reduce_grad: work item = (expert with copies, projection, chunk).
+struct ReduceArgs {
+  f32x4* gh[3];          // [E][row_vecs]
+  f32x4* rb[3];          // [R*B][row_vecs]
+  const int32_t* dup_n;
+  const int32_t* dup_e;
+  const int32_t* dup_first;
+  const int32_t* dup_cnt;
+  const int32_t* hold;
+  int64_t row_vecs;
+  int chunk_vecs, nchunks;
+};
+
+__global__ __launch_bounds__(kThreads) void reduce_grad_kernel(ReduceArgs a) {
+  const int n = *a.dup_n;
+  const int64_t items = (int64_t)n * 3 * a.nchunks;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int chunk = (int)(it % a.nchunks);
+    const int proj = (int)((it / a.nchunks) % 3);
+    const int q = (int)(it / ((int64_t)a.nchunks * 3));
+    const int e = a.dup_e[q];
+    const int first = a.dup_first[q];
+    const int cnt = a.dup_cnt[q];
+    f32x4* g = a.gh[proj] + (int64_t)e * a.row_vecs;
+    const int64_t v0 = (int64_t)chunk * a.chunk_vecs;
+    int64_t v1 = v0 + a.chunk_vecs;
+    if (v1 > a.row_vecs) v1 = a.row_vecs;
+    for (int64_t v = v0 + threadIdx.x; v < v1; v += kThreads) {
+      f32x4 acc = g[v];
+      for (int h = 0; h < cnt; ++h) {
+        f32x4* rbs = a.rb[proj] + (int64_t)a.hold[first + h] * a.row_vecs;
+        const f32x4 r = __builtin_nontemporal_load(rbs + v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __fadd_rn(acc[j], r[j]);
+        __builtin_nontemporal_store(zero, rbs + v);
+      }
+      g[v] = acc;
+    }
+  }
+}
+
+int capped_grid(const Ctx& c, int64_t want) {
+  int64_t cap = want;
+  if (c.d.num_cus > 0) cap = (int64_t)c.d.num_cus * 8;
+  if (want < cap) cap = want;
+  return (int)(cap < 1 ? 1 : cap);
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const Ctx& c, const moonep_plan_t& p, const uint16_t* x,
+                           int W, const float* rw, uint16_t* x_nvs, float* rw_nvs,
+                           hipStream_t s) {
+  const Dims& d = c.d;
+  DispatchArgs a;
+  a.x = (const u32x4*)x; a.rw = rw; a.x_nvs = (u32x4*)x_nvs; a.rw_nvs = rw_nvs;
+  a.dest = p.dest; a.cu = p.cu_seqlens; a.segn = p.seg_tokens; a.act = p.aux + d.aux.act;
+  a.ntok = d.R * d.S; a.K = d.K; a.nv = W / 8; a.EB = d.E + d.B; a.L2 = 2 * d.L;
+  a.tp = d.tp; a.NvS = (int)d.NvS;
+  a.pad_parts = (d.tp + 4 * kWaves - 1) / (4 * kWaves);
+  a.npad_blocks = d.R * a.L2 * a.pad_parts;
+  const int tok_blocks = capped_grid(c, (a.ntok + kWaves * 2 - 1) / (kWaves * 2));
+  dispatch_kernel<<<a.npad_blocks + tok_blocks, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Ctx& c, const moonep_plan_t& p, const uint16_t* y, int W,
+                          const float* rw_nvs, uint16_t* out, float* rw_sk, hipStream_t s) {
+  const Dims& d = c.d;
+  CombineArgs a;
+  a.y = (const u32x4*)y; a.rw_nvs = rw_nvs; a.out = (u32x4*)out; a.rw_sk = rw_sk;
+  a.dest = p.dest; a.ntok = d.R * d.S; a.K = d.K; a.nv = W / 8;
+  const int blocks = capped_grid(c, (a.ntok + kWaves - 1) / kWaves);
+  if (rw_nvs)
+    combine_kernel<true><<<blocks, kThreads, 0, s>>>(a);
+  else
+    combine_kernel<false><<<blocks, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefetch(const Ctx& c, const moonep_plan_t& p, const uint16_t* const home[3],
+                           uint16_t* const pool[3], hipStream_t s) {
+  const Dims& d = c.d;
+  PrefetchArgs a;
+  for (int i = 0; i < 3; ++i) {
+    a.home[i] = (const u32x4*)home[i];
+    a.pool[i] = (u32x4*)pool[i];
+  }
+  a.pf = p.prefetch_src;
+  a.aux_pf = p.aux + d.aux.pf;
+  a.aux_pf_n = p.aux + d.aux.pf_n;
+  a.row_vecs = (int64_t)d.H * d.Hp / 8;
+  a.chunk_vecs = kThreads * 4 * 16;   // 256 KiB per work item
+  a.nchunks = (int)((a.row_vecs + a.chunk_vecs - 1) / a.chunk_vecs);
+  const int64_t max_items = (int64_t)d.R * d.B * 3 * a.nchunks;
+  const int blocks = capped_grid(c, max_items < (int64_t)c.num_cu_device * 8
+                                        ? max_items : (int64_t)c.num_cu_device * 8);
+  prefetch_kernel<<<blocks, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_grad(const Ctx& c, const moonep_plan_t& p, float* const gh[3],
+                              float* const rb[3], hipStream_t s) {
+  const Dims& d = c.d;
+  ReduceArgs a;
+  for (int i = 0; i < 3; ++i) {
+    a.gh[i] = (f32x4*)gh[i];
+    a.rb[i] = (f32x4*)rb[i];
+  }
+  a.dup_n = p.aux + d.aux.dup_n;
+  a.dup_e = p.aux + d.aux.dup_e;
+  a.dup_first = p.aux + d.aux.dup_first;
+  a.dup_cnt = p.aux + d.aux.dup_cnt;
+  a.hold = p.aux + d.aux.hold;
+  a.row_vecs = (int64_t)d.H * d.Hp / 4;
+  a.chunk_vecs = kThreads * 16;      // 64 KiB of fp32 per work item
+  a.nchunks = (int)((a.row_vecs + a.chunk_vecs - 1) / a.chunk_vecs);
+  const int64_t max_items = (int64_t)d.R * d.B * 3 * a.nchunks;
+  const int blocks = capped_grid(c, max_items < (int64_t)c.num_cu_device * 8
+                                        ? max_items : (int64_t)c.num_cu_device * 8);
+  reduce_grad_kernel<<<blocks, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moonep

@@ -1,0 +1,224 @@
+/*
+ * moonep.h -- C ABI of the MoonEP hot path on AMD MI355X (gfx950).
+ *
+ * The operations are those of the MoonEP README (MoonshotAI/MoonEP mirror),
+ * section "API guide": a planner that makes every EP rank receive exactly
+ * S*K token slots, dispatch (fused permute), prefetch_weight, the grouped
+ * expert FFN over one [E+B,H,H'] weight tensor per projection addressed by
+ * cu_seqlens ("Usage > Integration > Weight buffer"), combine (fused
+ * unpermute) and reduce_grad ("Gradient buffer").
+ *
+ * One call serves all R EP ranks at once.  The ranks are R disjoint regions
+ * of the memory of one GPU: rank d's dispatched rows are rows
+ * [d*NvS, (d+1)*NvS) of every [R,NvS,...] array, and a "remote" store is a
+ * plain store into another rank's region.
+ *
+ * Conventions for every entry point:
+ *  - every pointer is a DEVICE pointer, allocated and owned by the caller,
+ *    unless the comment says host;
+ *  - bf16 values are passed as their 16-bit patterns (uint16_t);
+ *  - every array is dense row-major with the shape given in brackets;
+ *  - all work is enqueued on `stream`; no call synchronises the host except
+ *    moonep_read_stats;
+ *  - host-side argument checks run before anything is enqueued; on any error
+ *    nothing is enqueued and a nonzero moonep_status_t comes back;
+ *  - a routing the pages do not allow (expert id outside [0,E) or one expert
+ *    twice in a token) is found on the device: it sets a sticky flag in
+ *    stats[MOONEP_STAT_ERROR] and the plan becomes a safe no-op plan (every
+ *    token keeps a slot in its own rank's region, no segment, no prefetch),
+ *    so that later calls stay in bounds; read it with moonep_read_stats;
+ *  - one handle serves one stream at a time (it owns plan scratch).
+ */
+#ifndef MOONEP_H
+#define MOONEP_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOONEP_ABI_VERSION 1
+
+typedef int32_t moonep_status_t;
+enum {
+  MOONEP_OK = 0,
+  MOONEP_ERR_ARG = 1,     /* null / misaligned pointer, bad width or rank  */
+  MOONEP_ERR_CONFIG = 2,  /* configuration outside the supported range     */
+  MOONEP_ERR_MODE = 3,    /* training call with B != E/R                   */
+  MOONEP_ERR_HIP = 4,     /* a HIP runtime call or kernel launch failed    */
+  MOONEP_ERR_NOMEM = 5    /* scratch allocation in moonep_create failed    */
+};
+
+/* Problem sizes, in the README's notation ("Usage > Integration"):
+ * R EP ranks, S tokens per rank, top-K experts per token, E routed experts
+ * (E/R homed on each rank), B prefetch slots per rank, hidden size H, expert
+ * FFN size Hp (H'), token_padding the row-length granularity of cu_seqlens.
+ * num_cus: 0 = use the whole GPU for the data-movement kernels, else an
+ * upper bound on their workgroups in flight (the README's num_sms knob).
+ * Supported: 1 <= R <= 64, E % R == 0, E <= 1024, R*E <= 16384, 1 <= K <= min(E, 32),
+ * 1 <= S, R*S*K < 2^31, 0 <= B <= E/R, R*(E+B) <= 16384,
+ * token_padding >= 1, H % 64 == 0, Hp % 64 == 0, R*NvS*max(H,Hp) < 2^40. */
+typedef struct {
+  int32_t R, S, K, E, B, H, Hp, token_padding, num_cus;
+} moonep_config_t;
+
+typedef struct moonep_ctx* moonep_handle_t;
+
+/* Layout of the stats array of a plan (int32). */
+enum {
+  MOONEP_STAT_ERROR = 0,       /* sticky error bits, see MOONEP_ROUTE_*      */
+  MOONEP_STAT_DUPS = 1,        /* redundant experts: (rank, remote expert)   */
+  MOONEP_STAT_MAX_LOAD = 2,    /* max_e T_e                                  */
+  MOONEP_STAT_DONATIONS = 3,   /* donations made by the planner              */
+  MOONEP_STAT_PAD_ROWS = 4,    /* padding slots inside segments, all ranks   */
+  MOONEP_STAT_MAXVIO = 5,      /* maxvio as float32 bits                     */
+  MOONEP_STAT_REMOTE_GROUP = 8,/* [R] home group a rank duplicates from, -1  */
+  /* followed by [R] number of remote experts per rank                      */
+  MOONEP_STAT_FIXED = 8        /* stats length = MOONEP_STAT_FIXED + 2*R     */
+};
+enum {
+  MOONEP_ROUTE_ID_RANGE = 1,   /* an expert id outside [0, E)                */
+  MOONEP_ROUTE_REPEAT = 2,     /* one expert twice in one token              */
+  MOONEP_ROUTE_COUNTS = 4      /* tokens_per_expert disagrees with topk      */
+};
+
+/* The plan: caller-owned int32 device arrays, all written by moonep_plan and
+ * read by the other calls (the README's MoonEPCommPlan plus cu_seqlens).
+ * Sizes come from moonep_plan_len(). */
+typedef struct {
+  int32_t* counts;       /* [R,E]   tokens of rank r routed to expert e      */
+  int32_t* dest;         /* [R,S,K] global slot d*NvS+i of token (r,s,k)     */
+  int32_t* src;          /* [R,NvS] (r*S+s)*K+k held by a slot, -1 = none    */
+  int32_t* cu_seqlens;   /* [R,E+B] inclusive padded end offset of each row  */
+  int32_t* seg_tokens;   /* [R,E+B] real tokens in each row                  */
+  int32_t* prefetch_src; /* [R,B]   home expert copied into prefetch slot j  */
+  int32_t* stats;        /* [MOONEP_STAT_FIXED + 2R]                         */
+  int32_t* aux;          /* derived tables used by the other calls           */
+} moonep_plan_t;
+
+enum {
+  MOONEP_PLAN_COUNTS = 0, MOONEP_PLAN_DEST, MOONEP_PLAN_SRC,
+  MOONEP_PLAN_CU_SEQLENS, MOONEP_PLAN_SEG_TOKENS, MOONEP_PLAN_PREFETCH_SRC,
+  MOONEP_PLAN_STATS, MOONEP_PLAN_AUX, MOONEP_PLAN_NARRAYS
+};
+
+int32_t moonep_abi_version(void);
+const char* moonep_status_string(moonep_status_t status);
+
+/* Token slots per rank: S*K real slots plus the padding of at most 2*E/R
+ * active rows (E/R home rows and the rows of at most one remote home group,
+ * README "How to set B"), each padded by less than token_padding:
+ * NvS = S*K + 2*(E/R)*token_padding.  Returns -1 for an invalid config. */
+int64_t moonep_nvs(const moonep_config_t* cfg);
+
+/* Number of int32 elements of plan array `which` (MOONEP_PLAN_*), -1 on an
+ * invalid config or index. */
+int64_t moonep_plan_len(const moonep_config_t* cfg, int32_t which);
+
+/* Validate cfg (host) and allocate the handle's scratch on the current
+ * device (the README's Buffer(...)).  *out is untouched on error. */
+moonep_status_t moonep_create(const moonep_config_t* cfg, moonep_handle_t* out);
+/* Free the scratch (the README's buffer.destroy()).  NULL is a no-op. */
+moonep_status_t moonep_destroy(moonep_handle_t h);
+
+/* Plan (README "API guide > dispatch fwd", planning part).
+ * topk [R,S,K] int32 expert ids, k in the router's order.
+ * tokens_per_expert [R,E] int32 local counts, or NULL; when given it is
+ * checked against topk (MOONEP_ROUTE_COUNTS on mismatch).
+ * Writes every array of *plan.  Planning follows the spec P1-P9: group loads,
+ * chain-greedy donations that give every rank exactly S*K slots with at most
+ * one remote home group, expert lines sorted by (load, id), tokens of an
+ * expert in (rank, token) order, rows E..E+B-1 for the first B remote
+ * experts in ascending id and home rows for the rest, rows padded to
+ * token_padding. */
+moonep_status_t moonep_plan(moonep_handle_t h, const int32_t* topk,
+                            const int32_t* tokens_per_expert,
+                            const moonep_plan_t* plan, hipStream_t stream);
+
+/* Dispatch (README "API guide > dispatch fwd"; also "combine bwd", which is a
+ * re-dispatch of the output gradient with the saved plan).
+ * x [R,S,W] bf16 rows, W % 8 == 0 (W = H forward, W = H' or H for gradients).
+ * rw [R,S,K] fp32 route weights or NULL.
+ * Writes x_nvs [R,NvS,W]: slot dest[r,s,k] gets a bit copy of row x[r,s];
+ * padding slots inside a segment get zeros; slots past a rank's last segment
+ * are not written.  rw_nvs [R,NvS] (or NULL iff rw is NULL) gets rw[r,s,k]
+ * at the same slots and 0 at padding slots. */
+moonep_status_t moonep_dispatch(moonep_handle_t h, const moonep_plan_t* plan,
+                                const uint16_t* x, int32_t W, const float* rw,
+                                uint16_t* x_nvs, float* rw_nvs,
+                                hipStream_t stream);
+
+/* Combine (README "API guide > combine fwd"; also "dispatch bwd" when
+ * rw_nvs is NULL).  y_nvs [R,NvS,W] bf16, W % 8 == 0.
+ * out[r,s,:] = bf16_rne(acc) with acc = p_0 then acc = acc + p_k for
+ * k = 1..K-1 in fp32 round-to-nearest, p_k = rw_nvs[slot_k] * y_nvs[slot_k]
+ * (fp32 product, no fused multiply-add) or y_nvs[slot_k] if rw_nvs is NULL.
+ * rw_sk [R,S,K] (or NULL) gets rw_nvs[slot_k] (requires rw_nvs). */
+moonep_status_t moonep_combine(moonep_handle_t h, const moonep_plan_t* plan,
+                               const uint16_t* y_nvs, int32_t W,
+                               const float* rw_nvs, uint16_t* out,
+                               float* rw_sk, hipStream_t stream);
+
+/* Prefetch (README "API guide > dispatch fwd", prefetch_weight; "Weight
+ * buffer").  home[p] [E,H,Hp] bf16 for p = gate, up, down; pool[p]
+ * [R,B,H,Hp]: pool[p][d][j] becomes a bit copy of home[p][prefetch_src[d][j]]
+ * for every used slot; unused slots are not written.  Row i of rank d's
+ * [E+B,H,Hp] view is home[p]+i*H*Hp for i < E, else pool[p]+(d*B+i-E)*H*Hp.
+ * Pointer arrays home/pool are HOST arrays of 3 device pointers. */
+moonep_status_t moonep_prefetch_weight(moonep_handle_t h,
+                                       const moonep_plan_t* plan,
+                                       const uint16_t* const home[3],
+                                       uint16_t* const pool[3],
+                                       hipStream_t stream);
+
+/* Grouped SwiGLU expert FFN (README "Usage > Integration"): for rank d
+ * (rank = -1: all ranks) and every row i with cu_seqlens length > 0, over the
+ * row's padded segment X of x_nvs [R,NvS,H]:
+ *   G = X Wg_i, U = X Wu_i (bf16 MFMA, fp32 accumulation),
+ *   Z = bf16_rne(silu(G) * U) -> z_ws [R,NvS,Hp],
+ *   Y = bf16_rne(Z Wd_i^T)    -> y_nvs [R,NvS,H],
+ * with every projection stored [H,Hp] and rows resolved as in
+ * moonep_prefetch_weight.  y_nvs may equal x_nvs (in-place, the README's
+ * zero_copy); no other aliasing.  Slots outside segments are not written. */
+moonep_status_t moonep_expert_ffn(moonep_handle_t h, const moonep_plan_t* plan,
+                                  int32_t rank, const uint16_t* x_nvs,
+                                  const uint16_t* const home[3],
+                                  const uint16_t* const pool[3],
+                                  uint16_t* z_ws, uint16_t* y_nvs,
+                                  hipStream_t stream);
+
+/* Weight gradient of one projection (README "Gradient buffer"): for rank d
+ * (-1: all) and every row i with length > 0, dW_i += A_seg^T B_seg in fp32,
+ * A = a_nvs [R,NvS,H] bf16, B = b_nvs [R,NvS,Hp] bf16 (gate/up: A = x,
+ * B = dG or dU; down: A = dY, B = Z).  Row i < E is grad_home [E,H,Hp] fp32
+ * row i; row i >= E is reduce_buf [R,B,H,Hp] fp32 slot (d, i-E).  Training
+ * only: MOONEP_ERR_MODE unless B == E/R. */
+moonep_status_t moonep_expert_wgrad(moonep_handle_t h,
+                                    const moonep_plan_t* plan, int32_t rank,
+                                    const uint16_t* a_nvs,
+                                    const uint16_t* b_nvs, float* grad_home,
+                                    float* reduce_buf, hipStream_t stream);
+
+/* reduce_grad (README "Gradient buffer", "API guide > dispatch bwd"): for
+ * every home expert e and every used slot (d,j) with prefetch_src[d][j] == e,
+ * in ascending d: grad_home[p][e] += reduce_buf[p][d][j] (fp32
+ * round-to-nearest, no fused operations), then reduce_buf[p][d][j] = 0, for
+ * p = gate, up, down.  HOST arrays of 3 device pointers.  Training only:
+ * MOONEP_ERR_MODE unless B == E/R. */
+moonep_status_t moonep_reduce_grad(moonep_handle_t h,
+                                   const moonep_plan_t* plan,
+                                   float* const grad_home[3],
+                                   float* const reduce_buf[3],
+                                   hipStream_t stream);
+
+/* Synchronise `stream` and copy the plan's stats array to host_stats
+ * (MOONEP_STAT_FIXED + 2R int32, HOST memory).  For tests and reports. */
+moonep_status_t moonep_read_stats(moonep_handle_t h, const moonep_plan_t* plan,
+                                  int32_t* host_stats, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOONEP_H */

@@ -30,14 +30,14 @@ independently of the planner, and dense per-expert gradients.
 from .bf16 import bf16_to_f32, f32_to_bf16, f64_to_bf16
 from .maxvio import expert_loads, maxvio
 from .planner import Plan, nvs, plan
-from .moe import (combine, dispatch, expert_ffn, prefetch_weight, reduce_grad,
+from .moe import (combine, combine_rows, dispatch, expert_ffn, prefetch_weight, reduce_grad,
                   expert_wgrad, resolve_row)
 from .dense import dense_moe, dense_expert_grad, ffn_token
 from .bruteforce import min_duplicates
 
 __all__ = [
     "bf16_to_f32", "f32_to_bf16", "f64_to_bf16", "expert_loads", "maxvio",
-    "Plan", "nvs", "plan", "dispatch", "combine", "prefetch_weight",
+    "Plan", "nvs", "plan", "dispatch", "combine", "combine_rows", "prefetch_weight",
     "expert_ffn", "expert_wgrad", "reduce_grad", "resolve_row", "dense_moe",
     "dense_expert_grad", "ffn_token", "min_duplicates",
 ]

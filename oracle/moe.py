@@ -51,21 +51,29 @@ def dispatch(plan, x: np.ndarray, rw=None):
     return x_nvs, rw_nvs
 
 
-def combine(plan, y_nvs: np.ndarray, rw_nvs=None):
-    """y_nvs [R,NvS,W] bf16 bits -> out [R,S,W] bf16 bits (+ gathered rw)."""
-    R, S, K, NvS = plan.R, plan.S, plan.K, plan.NvS
-    W = y_nvs.shape[-1]
-    flat = y_nvs.reshape(R * NvS, W)
+def combine_rows(y_k: np.ndarray, w_k=None) -> np.ndarray:
+    """The per-token combine sum: y_k [..., K, W] bf16 bits, w_k [..., K]
+    fp32 or None -> [..., W] bf16 bits."""
+    K = y_k.shape[-2]
     acc = None
     for k in range(K):
-        yk = bf16_to_f32(flat[plan.dest[:, :, k]])            # [R,S,W]
-        if rw_nvs is not None:
-            wk = rw_nvs.reshape(-1)[plan.dest[:, :, k]][..., None]
-            pk = (wk.astype(np.float32) * yk).astype(np.float32)
+        yk = bf16_to_f32(y_k[..., k, :])
+        if w_k is not None:
+            pk = (np.asarray(w_k[..., k:k + 1], np.float32) * yk).astype(np.float32)
         else:
             pk = yk
         acc = pk if acc is None else (acc + pk).astype(np.float32)
-    out = f32_to_bf16(acc)
+    return f32_to_bf16(acc)
+
+
+def combine(plan, y_nvs: np.ndarray, rw_nvs=None):
+    """y_nvs [R,NvS,W] bf16 bits -> out [R,S,W] bf16 bits (+ gathered rw)."""
+    R, NvS = plan.R, plan.NvS
+    W = y_nvs.shape[-1]
+    flat = y_nvs.reshape(R * NvS, W)
+    y_k = flat[plan.dest]                                      # [R,S,K,W]
+    w_k = rw_nvs.reshape(-1)[plan.dest] if rw_nvs is not None else None
+    out = combine_rows(y_k, w_k)
     gathered = None
     if rw_nvs is not None:
         gathered = rw_nvs.reshape(-1)[plan.dest].astype(np.float32)

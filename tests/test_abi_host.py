@@ -1,0 +1,93 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/moonep.h declares, sizes its buffers as the oracle
+does, and rejects bad configurations and arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moonep_synth as synth
+import oracle
+from grouped_gemm_moonep_amd import _abi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "moonep.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moonep_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    lib = _abi.lib()
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    lib = _abi.lib()
+    assert lib.moonep_abi_version() == 1
+    for s in range(6):
+        assert _abi.status_string(s)
+    assert _abi.status_string(99) == "unknown status"
+
+
+def _cfg(w, **kw):
+    d = dict(R=w.R, S=w.S, K=w.K, E=w.E, B=w.B, H=w.H, Hp=w.Hp,
+             token_padding=w.token_padding, num_cus=0)
+    d.update(kw)
+    return _abi.config(**d)
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_nvs_and_plan_sizes_match_oracle(name):
+    w = synth.WORKLOADS[name]
+    cfg = _cfg(w)
+    NvS = oracle.nvs(w.S, w.K, w.E, w.R, w.token_padding)
+    assert _abi.nvs(cfg) == NvS
+    want = [w.R * w.E, w.R * w.S * w.K, w.R * NvS, w.R * (w.E + w.B), w.R * (w.E + w.B),
+            w.R * w.B, 8 + 2 * w.R]
+    got = [_abi.plan_len(cfg, i) for i in range(7)]
+    assert got == want
+    assert _abi.plan_len(cfg, 7) > 0
+    assert _abi.plan_len(cfg, 8) == -1
+
+
+BAD = [dict(E=6, R=4), dict(K=0), dict(K=9, E=8), dict(B=3), dict(B=-1), dict(S=0),
+       dict(token_padding=0), dict(H=100), dict(Hp=32), dict(R=65, E=130), dict(E=2048, R=2),
+       dict(num_cus=-1), dict(K=33, E=64)]
+
+
+@pytest.mark.parametrize("bad", BAD)
+def test_bad_config_rejected_on_host(bad):
+    w = synth.WORKLOADS["tiny_r4_s64_k2_e8"]
+    cfg = _cfg(w, **bad)
+    lib = _abi.lib()
+    assert lib.moonep_nvs(ctypes.byref(cfg)) == -1
+    h = ctypes.c_void_p()
+    assert lib.moonep_create(ctypes.byref(cfg), ctypes.byref(h)) == _abi.MOONEP_ERR_CONFIG
+    assert not h.value
+
+
+def test_null_arguments_rejected_on_host():
+    lib = _abi.lib()
+    plan = _abi.MoonepPlan()
+    P3 = ctypes.c_void_p * 3
+    ERR = _abi.MOONEP_ERR_ARG
+    assert lib.moonep_create(None, None) == ERR
+    assert lib.moonep_destroy(None) == _abi.MOONEP_OK
+    assert lib.moonep_plan(None, None, None, ctypes.byref(plan), None) == ERR
+    assert lib.moonep_dispatch(None, ctypes.byref(plan), None, 8, None, None, None, None) == ERR
+    assert lib.moonep_combine(None, ctypes.byref(plan), None, 8, None, None, None, None) == ERR
+    assert lib.moonep_prefetch_weight(None, ctypes.byref(plan), P3(), P3(), None) == ERR
+    assert lib.moonep_expert_ffn(None, ctypes.byref(plan), -1, None, P3(), P3(), None, None,
+                                 None) == ERR
+    assert lib.moonep_expert_wgrad(None, ctypes.byref(plan), -1, None, None, None, None,
+                                   None) == ERR
+    assert lib.moonep_reduce_grad(None, ctypes.byref(plan), P3(), P3(), None) == ERR
+    assert lib.moonep_read_stats(None, ctypes.byref(plan), None, None) == ERR

@@ -1,0 +1,178 @@
+"""The grouped SwiGLU FFN and the whole forward path on the GPU.
+
+* moonep_expert_ffn against the oracle's grouped FFN (float64 products, bf16
+  Z and Y) on every segment: rel-L2 <= 1e-2 and max-abs <= 2e-2;
+* slots outside segments are not written; y may alias x (in place);
+* plan -> dispatch -> prefetch -> FFN -> combine against the dense,
+  unbalanced per-token MoE (no planner involved) at the same tolerance;
+* the full-size forward config checked on sampled rows of sampled segments.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moonep_synth as synth
+import oracle
+from gpu_util import assert_close_bf16, buffer_for, dev, dev_bf16, host_bf16, log
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0x7F7F
+
+
+def _setup(w, target):
+    topk, rw = synth.routing(w, target)
+    x = synth.hidden(w)
+    home_h = [synth.expert_weights_host(w, i) for i in range(3)]
+    return topk, rw, x, home_h
+
+
+def _pool_dev(w):
+    return [torch.zeros((w.R, w.B, w.H, w.Hp), dtype=torch.bfloat16, device="cuda")
+            for _ in range(3)]
+
+
+@pytest.mark.parametrize("name,target,ranks", [
+    ("tiny_r4_s64_k2_e8", 1.0, None), ("tiny_r4_s64_k2_e8", 0.0, None),
+    ("tiny_r4_s64_k2_e8", "adv", None),
+    ("mid_r8_s1024_k4_e32", 0.0, [0, 5]), ("mid_r8_s1024_k4_e32", 2.0, [0, 3, 7]),
+])
+def test_ffn_matches_oracle(name, target, ranks):
+    w = synth.WORKLOADS[name]
+    log(f"ffn {name} target={target}")
+    topk, rw, x, home_h = _setup(w, target)
+    p = oracle.plan(topk, w.E, w.B, w.token_padding)
+    x_nvs_h, _ = oracle.dispatch(p, x)
+    pool_h = [oracle.prefetch_weight(p, home_h[i], np.zeros((w.R, w.B, w.H, w.Hp), np.uint16))
+              for i in range(3)]
+    z_want, y_want = oracle.expert_ffn(p, x_nvs_h, home_h, pool_h, ranks=ranks)
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    home = [dev_bf16(h) for h in home_h]
+    pool = _pool_dev(w)
+    buf.prefetch_weight(plan, home, pool)
+    x_nvs = dev_bf16(x_nvs_h)
+    z = torch.full((w.R, buf.NvS, w.Hp), SENT, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    y = torch.full((w.R, buf.NvS, w.H), SENT, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    buf.expert_ffn(plan, x_nvs, home, pool, z, y)
+    zg, yg = host_bf16(z), host_bf16(y)
+    for d in (range(w.R) if ranks is None else ranks):
+        end = p.cu_seqlens[d, -1]
+        assert_close_bf16(zg[d, :end], z_want[d, :end], what=f"z rank {d}")
+        assert_close_bf16(yg[d, :end], y_want[d, :end], what=f"y rank {d}")
+        assert (yg[d, end:] == SENT).all() and (zg[d, end:] == SENT).all()
+        pad = p.src[d, :end] < 0
+        assert (yg[d, :end][pad] == 0).all()
+    buf.destroy()
+
+
+def test_ffn_single_rank_and_in_place():
+    w = synth.WORKLOADS["tiny_r4_s64_k2_e8"]
+    topk, rw, x, home_h = _setup(w, "adv")
+    p = oracle.plan(topk, w.E, w.B, w.token_padding)
+    x_nvs_h, _ = oracle.dispatch(p, x)
+    pool_h = [oracle.prefetch_weight(p, home_h[i], np.zeros((w.R, w.B, w.H, w.Hp), np.uint16))
+              for i in range(3)]
+    _, y_want = oracle.expert_ffn(p, x_nvs_h, home_h, pool_h)
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    home = [dev_bf16(h) for h in home_h]
+    pool = _pool_dev(w)
+    buf.prefetch_weight(plan, home, pool)
+    x_nvs = dev_bf16(x_nvs_h)
+    z = torch.empty((w.R, buf.NvS, w.Hp), dtype=torch.bfloat16, device="cuda")
+    for d in range(w.R):
+        buf.expert_ffn(plan, x_nvs, home, pool, z, x_nvs, rank=d)   # y aliases x
+    yg = host_bf16(x_nvs)
+    for d in range(w.R):
+        end = p.cu_seqlens[d, -1]
+        assert_close_bf16(yg[d, :end], y_want[d, :end], what=f"in-place rank {d}")
+    buf.destroy()
+
+
+@pytest.mark.parametrize("name,target", [
+    ("tiny_r4_s64_k2_e8", 1.0), ("tiny_r4_s64_k2_e8", 0.0), ("tiny_r4_s64_k2_e8", "adv"),
+    ("mid_r8_s1024_k4_e32", 1.0),
+])
+def test_forward_equals_dense_moe(name, target):
+    w = synth.WORKLOADS[name]
+    log(f"forward {name} target={target}")
+    topk, rw, x, home_h = _setup(w, target)
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    home = [dev_bf16(h) for h in home_h]
+    pool = _pool_dev(w)
+    x_nvs, rw_nvs = buf.dispatch(plan, dev_bf16(x), dev(rw))
+    buf.prefetch_weight(plan, home, pool)
+    z, y = buf.expert_ffn(plan, x_nvs, home, pool, y_nvs=x_nvs)
+    out, rw_sk = buf.combine(plan, y, rw_nvs)
+    got = host_bf16(out)
+    if name.startswith("mid"):
+        rows = np.random.default_rng(0).choice(w.R * w.S, 256, replace=False)
+        r_, s_ = rows // w.S, rows % w.S
+        want = oracle.dense_moe(topk[r_, s_][None], rw[r_, s_][None], x[r_, s_][None], home_h)[0]
+        assert_close_bf16(got[r_, s_], want, what="forward sampled")
+    else:
+        want = oracle.dense_moe(topk, rw, x, home_h)
+        assert_close_bf16(got, want, what="forward")
+    assert np.array_equal(rw_sk.cpu().numpy(), rw)
+    buf.destroy()
+
+
+def test_inference_overflow_forward():
+    """B < E/R: overflow experts read their home rows through cu_seqlens."""
+    w = synth.Workload("infer_small", R=4, S=64, K=4, E=32, B=1, H=128, Hp=128,
+                       token_padding=16)
+    topk, rw = synth.routing_zipf(w, 1.5)
+    x = synth.hidden(w)
+    home_h = [synth.expert_weights_host(w, i) for i in range(3)]
+    p = oracle.plan(topk, w.E, w.B, w.token_padding)
+    assert max(len(r) for r in p.remote_experts) > w.B
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    home = [dev_bf16(h) for h in home_h]
+    pool = _pool_dev(w)
+    x_nvs, rw_nvs = buf.dispatch(plan, dev_bf16(x), dev(rw))
+    buf.prefetch_weight(plan, home, pool)
+    _, y = buf.expert_ffn(plan, x_nvs, home, pool)
+    out, _ = buf.combine(plan, y, rw_nvs)
+    assert_close_bf16(host_bf16(out), oracle.dense_moe(topk, rw, x, home_h), what="overflow")
+    buf.destroy()
+
+
+@pytest.mark.parametrize("name,target", [("fwd_r8_s4096_k8_e256", 2.0),
+                                         ("infer_r8_s128_k8_e256_b4", 4.0)])
+def test_ffn_full_size_sampled(name, target):
+    """Full-size weights drawn on the GPU; the oracle recomputes sampled rows
+    of sampled segments token by token from the home weights."""
+    w = synth.WORKLOADS[name]
+    log(f"ffn full size {name} target={target}")
+    topk, rw = synth.routing(w, target)
+    p = oracle.plan(topk, w.E, w.B, w.token_padding)
+    home = [torch.empty((w.E, w.H, w.Hp), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    for i in range(3):
+        synth.expert_weights_device(w, i, home[i])
+    pool = _pool_dev(w)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    x = torch.randn((w.R, w.S, w.H), generator=g, device="cuda").to(torch.bfloat16)
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    x_nvs, _ = buf.dispatch(plan, x)
+    buf.prefetch_weight(plan, home, pool)
+    z, y = buf.expert_ffn(plan, x_nvs, home, pool)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    segs = [(d, row) for d in range(w.R) for row in range(w.E + w.B) if p.seg_tokens[d, row] > 0]
+    pick = [segs[i] for i in rng.choice(len(segs), min(6, len(segs)), replace=False)]
+    xs = host_bf16(x).reshape(-1, w.H)
+    for d, row in pick:
+        e = row if row < w.E else p.prefetch_src[d, row - w.E]
+        end = p.cu_seqlens[d, row]
+        start = end - p.seg_len[d, row]
+        slots = start + rng.choice(p.seg_tokens[d, row], min(16, p.seg_tokens[d, row]), replace=False)
+        toks = p.src[d, slots] // w.K
+        wts = [host_bf16(home[i][e]) for i in range(3)]
+        zw, yw = oracle.ffn_token(xs[toks], *wts)
+        assert_close_bf16(host_bf16(z[d, slots]), zw, what=f"z d={d} row={row}")
+        assert_close_bf16(host_bf16(y[d, slots]), yw, what=f"y d={d} row={row}")
+    buf.destroy()
