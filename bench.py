@@ -1,0 +1,221 @@
+"""Benchmark of the MoonEP hot path on one MI355X.
+
+One step = one forward pass of the whole path over one batch of synthetic
+routing for the 8-rank, S=4096, K=8, E=256 (B=32), H=7168, H'=2048,
+token_padding=128 workload: plan -> dispatch -> prefetch_weight ->
+grouped SwiGLU FFN (all 8 ranks) -> combine.  The timed steps cycle through
+the imbalance sweep maxvio in {0, 0.5, 1, 2, 4, all-on-experts-0..7 (31)};
+inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is plan+dispatch+combine GB/s (algorithmic
+bytes over the summed stage times, HIP events on the launch stream); the
+grouped-GEMM TFLOP/s, the per-maxvio breakdown, the roofline of the dominant
+kernel (the grouped FFN GEMM) and of dispatch/combine, and the CPU oracle
+timed on a bounded sample are reported alongside.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, REPO)
+
+import moonep_synth as synth  # noqa: E402
+
+WORKLOAD = "fwd_r8_s4096_k8_e256"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def alg_bytes(w):
+    """Algorithmic bytes per call (padding and its zero-fill not counted)."""
+    R, S, K, E, B, H = w.R, w.S, w.K, w.E, w.B, w.H
+    ntok = R * S
+    plan = 8 * ntok * K + 4 * R * (E + B)              # topk in, dest out, cu_seqlens
+    dispatch = ntok * (2 * H + 2 * H * K + 12 * K)     # row once in, K rows out, rw + dest
+    combine = ntok * (2 * H * K + 2 * H + 12 * K)      # K rows in, row out, dest + rw in/out
+    return plan, dispatch, combine
+
+
+def ffn_flops(w):
+    return 6.0 * w.H * w.Hp * w.R * w.S * w.K
+
+
+def cpu_baseline(w, topk, rw, width=512):
+    """The oracle on the host: full plan of the headline routing, dispatch and
+    combine of a `width`-column slice of the hidden states."""
+    import oracle
+    os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")
+    x = synth.hidden(synth.Workload(**{**w.as_dict(), "H": width}))
+    t0 = time.perf_counter()
+    p = oracle.plan(topk, w.E, w.B, w.token_padding)
+    t1 = time.perf_counter()
+    x_nvs, rw_nvs = oracle.dispatch(p, x, rw)
+    t2 = time.perf_counter()
+    oracle.combine(p, x_nvs, rw_nvs)
+    t3 = time.perf_counter()
+    ws = synth.Workload(**{**w.as_dict(), "H": width})
+    pb, db, cb = alg_bytes(ws)
+    gbs = (pb + db + cb) / (t3 - t0) / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"plan of the full {w.name} routing at maxvio 1 + dispatch/combine "
+                      f"of a {width}-column slice of the hidden states (bytes scaled to "
+                      f"that slice); numpy, one thread",
+            "seconds": {"plan": round(t1 - t0, 3), "dispatch": round(t2 - t1, 3),
+                        "combine": round(t3 - t2, 3)}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=12)
+    ap.add_argument("--warmup", type=int, default=6)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--targets", default="0,0.5,1,2,4,adv")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the R EP ranks are emulated as R regions "
+              f"of one GPU's HBM); --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from grouped_gemm_moonep_amd import Buffer
+
+    w = synth.WORKLOADS[WORKLOAD]
+    dev = "cuda"
+    targets = [t if t == "adv" else float(t) for t in args.targets.split(",")]
+    print(f"[bench] {WORKLOAD}: generating routing for {targets}", file=sys.stderr, flush=True)
+    batches = []
+    host_routing = {}
+    for t in targets:
+        topk, rw = synth.routing(w, t)
+        host_routing[t] = (topk, rw)
+        batches.append((t, torch.from_numpy(topk).to(dev), torch.from_numpy(rw).to(dev)))
+
+    print("[bench] drawing weights and hidden states on the GPU", file=sys.stderr, flush=True)
+    home = [torch.empty((w.E, w.H, w.Hp), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    for i in range(3):
+        synth.expert_weights_device(w, i, home[i])
+    pool = [torch.zeros((w.R, w.B, w.H, w.Hp), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    g = torch.Generator(device=dev).manual_seed(0)
+    x = torch.randn((w.R, w.S, w.H), generator=g, device=dev).to(torch.bfloat16)
+
+    buf = Buffer(R=w.R, S=w.S, K=w.K, E=w.E, B=w.B, H=w.H, Hp=w.Hp,
+                 token_padding=w.token_padding)
+    plan = buf.new_plan()
+    x_nvs = torch.empty((w.R, buf.NvS, w.H), dtype=torch.bfloat16, device=dev)
+    rw_nvs = torch.empty((w.R, buf.NvS), dtype=torch.float32, device=dev)
+    z_ws = torch.empty((w.R, buf.NvS, w.Hp), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((w.R, w.S, w.H), dtype=torch.bfloat16, device=dev)
+    rw_sk = torch.empty((w.R, w.S, w.K), dtype=torch.float32, device=dev)
+
+    def step(i, ev=None):
+        t, topk, rw = batches[i % len(batches)]
+        rec = (lambda j: ev[j].record()) if ev is not None else (lambda j: None)
+        rec(0)
+        buf.plan(topk, plan=plan)
+        rec(1)
+        buf.dispatch(plan, x, rw, x_nvs=x_nvs, rw_nvs=rw_nvs)
+        rec(2)
+        buf.prefetch_weight(plan, home, pool)
+        rec(3)
+        buf.expert_ffn(plan, x_nvs, home, pool, z_ws, x_nvs)      # in place (zero copy)
+        rec(4)
+        buf.combine(plan, x_nvs, rw_nvs, out=out, rw_sk=rw_sk)
+        rec(5)
+        return t
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # per-maxvio stats (duplicates, realized imbalance) from the GPU plan
+    stats = {}
+    for t, topk, _ in batches:
+        buf.plan(topk, plan=plan)
+        st = buf.read_stats(plan)
+        stats[t] = {"dups": int(st[1]), "maxvio": float(np.int32(st[5]).view(np.float32)),
+                    "pad_rows": int(st[4])}
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    used = []
+    for i in range(args.steps):
+        used.append(step(i, events[i]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["plan", "dispatch", "prefetch", "ffn", "combine"]
+    per = {n: [] for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)     # seconds
+    pb, db, cb = alg_bytes(w)
+    t_pdc = sum(per["plan"]) + sum(per["dispatch"]) + sum(per["combine"])
+    gbs = args.steps * (pb + db + cb) / t_pdc / 1e9
+    t_ffn = float(np.mean(per["ffn"]))
+    tflops = ffn_flops(w) / t_ffn / 1e12
+    t_disp = float(np.mean(per["dispatch"]))
+    t_comb = float(np.mean(per["combine"]))
+
+    sweep = {}
+    for t in targets:
+        idx = [i for i, u in enumerate(used) if u == t]
+        if not idx:
+            continue
+        m = lambda n: float(np.mean([per[n][i] for i in idx]))
+        sweep[str(t)] = {
+            "realized_maxvio": round(stats[t]["maxvio"], 4), "dups": stats[t]["dups"],
+            "pad_rows": stats[t]["pad_rows"],
+            "plan_us": round(m("plan") * 1e6, 2), "dispatch_us": round(m("dispatch") * 1e6, 1),
+            "prefetch_us": round(m("prefetch") * 1e6, 1), "ffn_ms": round(m("ffn") * 1e3, 3),
+            "combine_us": round(m("combine") * 1e6, 1),
+            "pdc_GBps": round((pb + db + cb) / (m("plan") + m("dispatch") + m("combine")) / 1e9, 1),
+            "gemm_TFLOPs": round(ffn_flops(w) / m("ffn") / 1e12, 1),
+        }
+
+    result = {
+        "metric": "plan+dispatch+combine GB/s, grouped-GEMM TFLOP/s vs maxvio, 1 rank",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Zipf-biased top-K routing, N(0,1) hidden, N(0,0.02) weights)",
+        "config": {"workload": WORKLOAD, "R": w.R, "S": w.S, "K": w.K, "E": w.E, "B": w.B,
+                   "H": w.H, "Hp": w.Hp, "token_padding": w.token_padding,
+                   "maxvio_targets": [str(t) for t in targets],
+                   "step": "plan, dispatch, prefetch_weight, grouped SwiGLU FFN (8 ranks), combine"},
+        "gemm_tflops": round(tflops, 1),
+        "roofline": {"kernel": "grouped SwiGLU FFN (ffn_gateup + ffn_down, one call, 8 ranks)",
+                     "bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "per_launch": {"flops": ffn_flops(w), "avg_s": t_ffn}},
+        "roofline_dispatch": {"bound": "hbm", "achieved": round(db / t_disp / 1e9, 1),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(db / t_disp / 1e9 / HBM_PEAK_GBS, 4),
+                              "traffic": None, "per_launch": {"bytes": db, "avg_s": t_disp}},
+        "roofline_combine": {"bound": "hbm", "achieved": round(cb / t_comb / 1e9, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(cb / t_comb / 1e9 / HBM_PEAK_GBS, 4),
+                             "traffic": None, "per_launch": {"bytes": cb, "avg_s": t_comb}},
+        "sweep": sweep,
+    }
+    buf.destroy()
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        t1 = 1.0 if 1.0 in host_routing else targets[0]
+        result["cpu_baseline"] = cpu_baseline(w, *host_routing[t1])
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
