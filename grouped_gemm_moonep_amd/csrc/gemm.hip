@@ -21,12 +21,14 @@
 //
 // CDNA4 mapping: 256 threads = 4 waves in a 2x2 grid, each wave a 128x128
 // sub-tile as 4x4 v_mfma_f32_32x32x16_bf16 blocks (256 fp32 accumulators per
-// lane).  K advances 64 per step through two 64 KiB LDS stages (A rows and
-// B^T rows, 128 B each, 16-byte chunks XOR-swizzled by row so that MFMA
-// fragment reads are bank-conflict free); the next step's global loads are
-// in flight while the current step's MFMAs run.  Operands whose contraction
-// index is not contiguous in memory (gate/up weights, both wgrad operands)
-// are transposed 8x8 in registers (v_perm) on their way into LDS.
+// lane).  K advances 64 per step through two 72 KiB LDS stages (A rows and
+// B^T rows of 64 k, padded to 144 B so that MFMA fragment reads are
+// bank-conflict free).  Global loads are buffer loads
+// (out-of-range offsets read zero: no branches at tile edges), issued one
+// step ahead into registers; fragments are double-buffered in registers so
+// LDS latency hides behind MFMAs; one barrier per step.  Operands whose
+// contraction index is not contiguous in memory (gate/up weights, both wgrad
+// operands) are transposed 8x8 in registers (v_perm) on their way into LDS.
 // Workgroup ids are remapped so that every XCD (own L2) works through a
 // contiguous range of tiles: neighbouring tiles share weight or activation
 // slabs in that XCD's L2.
@@ -41,13 +43,16 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kTileBytes = 256 * BK * 2;          // 32 KiB: 256 rows x 128 B
+// LDS tile rows hold 64 k (128 B) padded to 144 B: 16 consecutive rows then
+// start in 16 different 16-byte bank groups, so the MFMA fragment reads (16
+// rows per 16-lane group) are conflict-free, and every address is a
+// per-thread base plus a compile-time offset.
+constexpr int kRowBytes = 144;
+constexpr int kTileBytes = 256 * kRowBytes;       // 36 KiB
 constexpr int kStageBytes = 2 * kTileBytes;       // A tile + B^T tile
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kRowBytes + chunk * 16; }
 
 __device__ __forceinline__ int round_up(int n, int m) { return (n + m - 1) / m * m; }
 
@@ -58,23 +63,56 @@ __device__ __forceinline__ unsigned bf16_rne(float f) {
 }
 
 // ---------------------------------------------------------------------------
+// Global loads go through buffer resources: an offset past num_records
+// returns zeros, so tile edges (segment end, matrix edge) need no branches.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOob = 0x80000000u;   // any offset >= num_records reads 0
+
+// The descriptor must live in scalar registers; base and size are made
+// provably wave-uniform (readfirstlane) so the compiler never wraps a load in
+// a per-lane loop over descriptors.
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  const uint32_t n = bytes > 0x7FFFFFFF ? 0x7FFFFFFFu : (uint32_t)bytes;
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* ub = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(n),
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 bload(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+// Stores past num_records are dropped: the epilogues need no branches.
+__device__ __forceinline__ void bstore16(Rsrc r, uint32_t voff, unsigned v) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, voff, 0, 0);
+}
+
 // Loader for an operand whose contraction index is contiguous: 256 tile rows
 // x 64 k.  Thread t covers chunk t%8 (8 k) of rows t/8 + 32 i.
 struct DirectTile {
+  static constexpr int kCommitValu = 0;   // VALU per LDS write in commit()
+  Rsrc rs;
+  uint32_t voff[8];
   u32x4 v[8];
-  __device__ __forceinline__ void load(const uint16_t* base, int64_t ld, int rows_valid,
-                                       int64_t k0) {
+  // base: row 0, k 0 of the tile; ld: row stride (elements)
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int rows_valid) {
     const int t = threadIdx.x, c = t & 7;
+    rs = make_rsrc(base, (int64_t)rows_valid * ld * 2);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = (t >> 3) + 32 * i;
-      if (r < rows_valid)
-        v[i] = *(const u32x4*)(base + (int64_t)r * ld + k0 + c * 8);
-      else
-        v[i] = u32x4{0u, 0u, 0u, 0u};
+      voff[i] = r < rows_valid ? (uint32_t)(r * ld * 2 + c * 16) : kOob;
     }
   }
-  __device__ __forceinline__ void store(char* tile) const {
+  // the whole offset goes in the VGPR operand: the hardware range check
+  // covers that operand, not the scalar offset
+  __device__ __forceinline__ void issue(int64_t k0) {
+    const uint32_t ko = (uint32_t)(k0 * 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = bload(rs, voff[i] + ko, 0);
+  }
+  __device__ __forceinline__ void commit(char* tile) const {
     const int t = threadIdx.x, c = t & 7;
 #pragma unroll
     for (int i = 0; i < 8; ++i) *(u32x4*)(tile + lds_off((t >> 3) + 32 * i, c)) = v[i];
@@ -82,31 +120,43 @@ struct DirectTile {
 };
 
 // Loader for an operand stored [k][n] (n contiguous): 64 k x 256 tile rows
-// (n).  Thread t covers n-chunk c = t%32 (8 n) and k-block kb = t/32 (8 k);
-// the 8x8 block is transposed in registers so that each tile row holds 8
-// consecutive k.  Rows [0,128) come from src0 and [128,256) from src1 (the
-// gate and up weights side by side); pass src1 = src0 + 128 for one matrix.
-// nv0 / nv1: valid columns of each half; k_valid: valid k rows.
+// (n).  Threads 0-127 fill tile rows [0,128) from src0, threads 128-255 rows
+// [128,256) from src1 (the gate and the up weights side by side, or two
+// column halves of one matrix), so every wave reads one matrix.  Thread t
+// covers k-block t%8 (8 k) and n-chunk (t/8)%16 (8 n); the 8x8 block is
+// transposed in registers so that each tile row holds 8 consecutive k.  With
+// k-blocks varying fastest, each 16-lane group of a transposed LDS write
+// covers 16 different bank groups.
 struct TransTile {
+  static constexpr int kCommitValu = 2;   // v_perm per LDS write (4 per 8, 2 loaders)
+  Rsrc rs;
+  uint32_t voff[8];
+  uint32_t ld2;
   u32x4 v[8];
-  __device__ __forceinline__ void load(const uint16_t* src0, const uint16_t* src1, int64_t ld,
-                                       int64_t k0, int k_valid, int nv0, int nv1) {
-    const int t = threadIdx.x, c = t & 31, kb = t >> 5;
-    const int half = c >> 4;
-    const int n = (c & 15) * 8;                 // within the half
+  // src0/src1: k 0, n 0 of each half; ld: k stride (elements); k_total: valid
+  // k rows from k 0; nv0/nv1: valid columns of each half
+  __device__ __forceinline__ void init(const uint16_t* src0, const uint16_t* src1, int64_t ld,
+                                       int64_t k_total, int nv0, int nv1) {
+    const int t = threadIdx.x, half = t >> 7;
+    const int kb = t & 7, n = ((t >> 3) & 15) * 8;
     const uint16_t* src = half ? src1 : src0;
-    const bool nok = n < (half ? nv1 : nv0);
+    const int nv = half ? nv1 : nv0;
+    rs = make_rsrc(src, k_total * ld * 2);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int k = kb * 8 + i;
-      if (nok && k < k_valid)
-        v[i] = *(const u32x4*)(src + (k0 + k) * ld + n);
-      else
-        v[i] = u32x4{0u, 0u, 0u, 0u};
+      voff[i] = n < nv ? (uint32_t)(k * ld * 2 + n * 2) : kOob;
     }
+    ld2 = (uint32_t)(ld * 2);
   }
-  __device__ __forceinline__ void store(char* tile) const {
-    const int t = threadIdx.x, c = t & 31, kb = t >> 5;
+  __device__ __forceinline__ void issue(int64_t k0) {
+    const uint32_t ko = (uint32_t)(k0 * ld2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = bload(rs, voff[i] + ko, 0);
+  }
+  __device__ __forceinline__ void commit(char* tile) const {
+    const int t = threadIdx.x, half = t >> 7;
+    const int kb = t & 7, c = (t >> 3) & 15;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int sel = (j & 1) ? 0x07060302 : 0x05040100;
@@ -114,31 +164,109 @@ struct TransTile {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         o[q] = __builtin_amdgcn_perm(v[2 * q + 1][j >> 1], v[2 * q][j >> 1], sel);
-      *(u32x4*)(tile + lds_off(c * 8 + j, kb)) = o;
+      *(u32x4*)(tile + lds_off(half * 128 + c * 8 + j, kb)) = o;
     }
   }
 };
 
-// One 64-deep step of MFMAs for a wave: A rows wm*128 + [0,128), B^T rows
-// nrow[j] + [0,32) for the 4 column blocks.
-__device__ __forceinline__ void mma_step(const char* A, const char* Bt, f32x16 acc[4][4], int arow0,
-                                         const int nrow[4]) {
+// MFMA fragments of one 16-deep sub-step for a wave: A rows arow0 + 32 i,
+// B^T rows nrow[j] (+ lane%32), k-chunk 2 kk + lane/32.
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+__device__ __forceinline__ void read_frags(Frags& f, const char* stage, int kk, int arow0,
+                                           const int nrow[4]) {
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
+  const char* A = stage;
+  const char* Bt = stage + kTileBytes;
 #pragma unroll
-  for (int kk = 0; kk < BK / 16; ++kk) {
-    bf16x8 a[4], b[4];
+  for (int i = 0; i < 4; ++i)
+    f.a[i] = *(const bf16x8*)(A + lds_off(arow0 + i * 32 + lr, 2 * kk + lh));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *(const bf16x8*)(A + lds_off(arow0 + i * 32 + lr, 2 * kk + lh));
+  for (int j = 0; j < 4; ++j)
+    f.b[j] = *(const bf16x8*)(Bt + lds_off(nrow[j] + lr, 2 * kk + lh));
+}
+
+__device__ __forceinline__ void mma16(f32x16 acc[4][4], const Frags& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      b[j] = *(const bf16x8*)(Bt + lds_off(nrow[j] + lr, 2 * kk + lh));
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Scheduling groups (LLVM AMDGPU sched_group_barrier masks).
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100, kSgDsWrite = 0x200;
+#define MOONEP_SG(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
+// One sub-step: 8 fragment reads for the next sub-step, then 16 MFMAs on the
+// current fragments (the reads' latency hides behind the MFMAs).
+#define MOONEP_SUBSTEP()      \
+  do {                        \
+    MOONEP_SG(kSgDsRead, 8);  \
+    MOONEP_SG(kSgMfma, 16);   \
+    __builtin_amdgcn_sched_barrier(0); \
+  } while (0)
+
+// The K loop shared by every GEMM here.  Two LDS stages; per 64-deep step:
+// the next step's global loads are issued first; sub-steps 0-2 each read the
+// following sub-step's fragments while 16 MFMAs run; during sub-step 2 the
+// loaded tiles are transposed / written to the other stage, interleaved one
+// LDS write per MFMA; one barrier; sub-step 3's MFMAs cover the read of the
+// next step's first fragments.  Scheduling barriers pin this order (left
+// alone, the compiler sinks the loads next to their consumers and exposes the
+// memory latency).  The last step is peeled.
+template <class TA, class TB>
+__device__ __forceinline__ void gemm_loop(TA& la, TB& lb, char* smem, int nk, f32x16 acc[4][4],
+                                          int arow0, const int nrow[4]) {
+  if (nk <= 0) return;
+  la.issue(0);
+  lb.issue(0);
+  la.commit(smem);
+  lb.commit(smem + kTileBytes);
+  __syncthreads();
+  Frags f0, f1;
+  read_frags(f0, smem, 0, arow0, nrow);
+  int kt = 0;
+  for (; kt + 1 < nk; ++kt) {
+    char* cur = smem + (kt & 1) * kStageBytes;
+    char* nxt = smem + ((kt + 1) & 1) * kStageBytes;
+    __builtin_amdgcn_sched_barrier(0);
+    la.issue((int64_t)(kt + 1) * BK);
+    lb.issue((int64_t)(kt + 1) * BK);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(f1, cur, 1, arow0, nrow);
+    mma16(acc, f0);
+    MOONEP_SUBSTEP();
+    read_frags(f0, cur, 2, arow0, nrow);
+    mma16(acc, f1);
+    MOONEP_SUBSTEP();
+    read_frags(f1, cur, 3, arow0, nrow);
+    mma16(acc, f0);
+    la.commit(nxt);
+    lb.commit(nxt + kTileBytes);
+    MOONEP_SG(kSgDsRead, 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 16; ++i) {
+      MOONEP_SG(kSgValu, TA::kCommitValu + TB::kCommitValu);
+      MOONEP_SG(kSgDsWrite, 1);
+      MOONEP_SG(kSgMfma, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    read_frags(f0, nxt, 0, arow0, nrow);
+    mma16(acc, f1);
+    MOONEP_SUBSTEP();
   }
+  char* cur = smem + (kt & 1) * kStageBytes;
+  read_frags(f1, cur, 1, arow0, nrow);
+  mma16(acc, f0);
+  read_frags(f0, cur, 2, arow0, nrow);
+  mma16(acc, f1);
+  read_frags(f1, cur, 3, arow0, nrow);
+  mma16(acc, f0);
+  mma16(acc, f1);
 }
 
 __device__ __forceinline__ void zero_acc(f32x16 acc[4][4]) {
@@ -181,13 +309,25 @@ __device__ __forceinline__ const uint16_t* weight_row(const FfnArgs& a, int p, i
   return row < a.E ? a.home[p] + (int64_t)row * rs : a.pool[p] + ((int64_t)d * a.B + row - a.E) * rs;
 }
 
+// Within a rank, tiles are taken in groups of kGroupM M-tiles: the group's
+// M-tiles for the first N-tile, then for the second, ...  Workgroups that run
+// together on an XCD (32 CUs) then cover kGroupM M-tiles x 32/kGroupM
+// N-tiles, so each weight slab in that XCD's L2 serves kGroupM workgroups and
+// each activation slab 32/kGroupM.
+constexpr int kGroupM = 4;
+
 __device__ __forceinline__ bool decode(const FfnArgs& a, int* d, Tile* tl, int* nt) {
   const int64_t lt = logical_tile();
-  const int64_t total = (int64_t)a.nranks * a.max_tiles * a.ntn;
+  const int64_t per_rank = (int64_t)a.max_tiles * a.ntn;
+  const int64_t total = (int64_t)a.nranks * per_rank;
   if (lt >= total) return false;
-  *nt = (int)(lt % a.ntn);
-  const int t = (int)((lt / a.ntn) % a.max_tiles);
-  *d = a.rank0 + (int)(lt / ((int64_t)a.ntn * a.max_tiles));
+  *d = a.rank0 + (int)(lt / per_rank);
+  const int l = (int)(lt % per_rank);
+  const int group = l / (kGroupM * a.ntn);
+  const int gm = min(kGroupM, a.max_tiles - group * kGroupM);   // M-tiles in this group
+  const int rem = l - group * kGroupM * a.ntn;
+  *nt = rem / gm;
+  const int t = group * kGroupM + rem % gm;
   if (t >= a.ntiles[*d]) return false;
   const int32_t* e = a.tiles + ((int64_t)*d * a.max_tiles + t) * 4;
   tl->row = e[0];
@@ -228,54 +368,37 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   if (!decode(a, &d, &tl, &nt)) return;
   const int n0 = nt * 128;
   const int rows_valid = tl.m1 - tl.m0;
-  const uint16_t* A = a.x + ((int64_t)d * a.NvS + tl.m0) * a.H;
-  const uint16_t* Wg = weight_row(a, 0, d, tl.row) + n0;
-  const uint16_t* Wu = weight_row(a, 1, d, tl.row) + n0;
   const int nvh = a.Hp - n0 < 128 ? a.Hp - n0 : 128;   // valid columns of each half
   const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int nrow[4] = {wn * 64, wn * 64 + 32, 128 + wn * 64, 128 + wn * 64 + 32};
 
-  f32x16 acc[4][4];
-  zero_acc(acc);
   DirectTile la;
   TransTile lb;
-  const int nk = a.H / BK;
-  la.load(A, a.H, rows_valid, 0);
-  lb.load(Wg, Wu, a.Hp, 0, BK, nvh, nvh);
-  la.store(smem);
-  lb.store(smem + kTileBytes);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * kStageBytes;
-    char* nxt = smem + ((kt + 1) & 1) * kStageBytes;
-    if (kt + 1 < nk) {
-      la.load(A, a.H, rows_valid, (int64_t)(kt + 1) * BK);
-      lb.load(Wg, Wu, a.Hp, (int64_t)(kt + 1) * BK, BK, nvh, nvh);
-    }
-    mma_step(cur, cur + kTileBytes, acc, wm * 128, nrow);
-    if (kt + 1 < nk) {
-      la.store(nxt);
-      lb.store(nxt + kTileBytes);
-    }
-    __syncthreads();
-  }
+  la.init(a.x + ((int64_t)d * a.NvS + tl.m0) * a.H, a.H, rows_valid);
+  lb.init(weight_row(a, 0, d, tl.row) + n0, weight_row(a, 1, d, tl.row) + n0, a.Hp, a.H, nvh,
+          nvh);
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  gemm_loop(la, lb, smem, a.H / BK, acc, wm * 128, nrow);
+
   // SwiGLU epilogue: blocks j = 0,1 are gate, j = 2,3 the matching up.
+  // Rows past the segment fall outside the store range; columns past H' get
+  // an out-of-range offset.
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
-  uint16_t* Z = a.z + ((int64_t)d * a.NvS + tl.m0) * a.Hp + n0;
+  const Rsrc zs = make_rsrc(a.z + ((int64_t)d * a.NvS + tl.m0) * a.Hp + n0,
+                            (int64_t)rows_valid * a.Hp * 2);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = wn * 64 + j * 32 + lr;
-      if (n0 + n >= a.Hp) continue;
+      const uint32_t col = n < nvh ? (uint32_t)(n * 2) : kOob;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = wm * 128 + i * 32 + acc_row(v, lh);
-        if (m < rows_valid) {
-          const float g = acc[i][j][v], u = acc[i][j + 2][v];
-          const float zz = g / (1.0f + __expf(-g)) * u;
-          Z[(int64_t)m * a.Hp + n] = (uint16_t)bf16_rne(zz);
-        }
+        const float g = acc[i][j][v], u = acc[i][j + 2][v];
+        const float zz = g / (1.0f + __expf(-g)) * u;
+        bstore16(zs, col + (uint32_t)(m * a.Hp * 2), bf16_rne(zz));
       }
     }
 }
@@ -289,47 +412,30 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   if (!decode(a, &d, &tl, &nt)) return;
   const int n0 = nt * BN;
   const int rows_valid = tl.m1 - tl.m0;
-  const uint16_t* A = a.z + ((int64_t)d * a.NvS + tl.m0) * a.Hp;
-  const uint16_t* Wd = weight_row(a, 2, d, tl.row) + (int64_t)n0 * a.Hp;
   const int cols_valid = a.H - n0 < BN ? a.H - n0 : BN;
   const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int nrow[4] = {wn * 128, wn * 128 + 32, wn * 128 + 64, wn * 128 + 96};
 
+  DirectTile la, lb;
+  la.init(a.z + ((int64_t)d * a.NvS + tl.m0) * a.Hp, a.Hp, rows_valid);
+  lb.init(weight_row(a, 2, d, tl.row) + (int64_t)n0 * a.Hp, a.Hp, cols_valid);
   f32x16 acc[4][4];
   zero_acc(acc);
-  DirectTile la, lb;
-  const int nk = a.Hp / BK;
-  la.load(A, a.Hp, rows_valid, 0);
-  lb.load(Wd, a.Hp, cols_valid, 0);
-  la.store(smem);
-  lb.store(smem + kTileBytes);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * kStageBytes;
-    char* nxt = smem + ((kt + 1) & 1) * kStageBytes;
-    if (kt + 1 < nk) {
-      la.load(A, a.Hp, rows_valid, (int64_t)(kt + 1) * BK);
-      lb.load(Wd, a.Hp, cols_valid, (int64_t)(kt + 1) * BK);
-    }
-    mma_step(cur, cur + kTileBytes, acc, wm * 128, nrow);
-    if (kt + 1 < nk) {
-      la.store(nxt);
-      lb.store(nxt + kTileBytes);
-    }
-    __syncthreads();
-  }
+  gemm_loop(la, lb, smem, a.Hp / BK, acc, wm * 128, nrow);
+
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
-  uint16_t* Y = a.y + ((int64_t)d * a.NvS + tl.m0) * a.H + n0;
+  const Rsrc ys = make_rsrc(a.y + ((int64_t)d * a.NvS + tl.m0) * a.H + n0,
+                            (int64_t)rows_valid * a.H * 2);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = nrow[j] + lr;
-      if (n >= cols_valid) continue;
+      const uint32_t col = n < cols_valid ? (uint32_t)(n * 2) : kOob;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = wm * 128 + i * 32 + acc_row(v, lh);
-        if (m < rows_valid) Y[(int64_t)m * a.H + n] = (uint16_t)bf16_rne(acc[i][j][v]);
+        bstore16(ys, col + (uint32_t)(m * a.H * 2), bf16_rne(acc[i][j][v]));
       }
     }
 }
@@ -373,49 +479,32 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int nrow[4] = {wn * 128, wn * 128 + 32, wn * 128 + 64, wn * 128 + 96};
 
+  TransTile la, lb;
+  la.init(A, A + 128, a.H, ntok, mv0, mv1);
+  lb.init(Bm, Bm + 128, a.Hp, ntok, nv0, nv1);
   f32x16 acc[4][4];
   zero_acc(acc);
-  TransTile la, lb;
-  const int nk = (ntok + BK - 1) / BK;
-  if (nk > 0) {
-    la.load(A, A + 128, a.H, 0, ntok, mv0, mv1);
-    lb.load(Bm, Bm + 128, a.Hp, 0, ntok, nv0, nv1);
-    la.store(smem);
-    lb.store(smem + kTileBytes);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * kStageBytes;
-    char* nxt = smem + ((kt + 1) & 1) * kStageBytes;
-    if (kt + 1 < nk) {
-      const int k0 = (kt + 1) * BK;
-      la.load(A, A + 128, a.H, k0, ntok - k0, mv0, mv1);
-      lb.load(Bm, Bm + 128, a.Hp, k0, ntok - k0, nv0, nv1);
-    }
-    mma_step(cur, cur + kTileBytes, acc, wm * 128, nrow);
-    if (kt + 1 < nk) {
-      la.store(nxt);
-      lb.store(nxt + kTileBytes);
-    }
-    __syncthreads();
-  }
+  gemm_loop(la, lb, smem, (ntok + BK - 1) / BK, acc, wm * 128, nrow);
+
+  // fp32 read-modify-write; rows past H and columns past H' are out of range
   const int64_t rs = (int64_t)a.H * a.Hp;
   float* G = (row < a.E ? a.gh + (int64_t)row * rs : a.rb + ((int64_t)d * a.B + row - a.E) * rs) +
              (int64_t)m0 * a.Hp + n0;
+  const Rsrc gs = make_rsrc(G, (int64_t)mv * a.Hp * 4);
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = nrow[j] + lr;
-      if (n >= nv) continue;
+      const uint32_t col = n < nv ? (uint32_t)(n * 4) : kOob;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = wm * 128 + i * 32 + acc_row(v, lh);
-        if (m < mv) {
-          float* p = G + (int64_t)m * a.Hp + n;
-          *p = __fadd_rn(*p, acc[i][j][v]);
-        }
+        const uint32_t off = col + (uint32_t)(m * a.Hp * 4);
+        const float old = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gs, off, 0, 0));
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, __fadd_rn(old, acc[i][j][v])),
+                                              gs, off, 0, 0);
       }
     }
 }
