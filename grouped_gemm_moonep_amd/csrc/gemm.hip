@@ -40,19 +40,18 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
-constexpr int BM = 256, BN = 256, BK = 64;
-// LDS tile rows hold 64 k (128 B) padded to 144 B: 16 consecutive rows then
-// start in 16 different 16-byte bank groups, so the MFMA fragment reads (16
-// rows per 16-lane group) are conflict-free, and every address is a
-// per-thread base plus a compile-time offset.
-constexpr int kRowBytes = 144;
-constexpr int kTileBytes = 256 * kRowBytes;       // 36 KiB
-constexpr int kStageBytes = 2 * kTileBytes;       // A tile + B^T tile
+constexpr int BM = 256, BN = 256, BK = 32;        // K advances 32 per step
+constexpr int kStages = 4;                        // LDS ring depth
+constexpr int kTileBytes = 256 * BK * 2;          // 16 KiB per operand tile
+constexpr int kStageBytes = 2 * kTileBytes;       // A tile + B tile
 constexpr int kXcds = 8;
+constexpr int kLoadsPerStep = 8;                  // LDS-DMA loads per wave per step
 
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kRowBytes + chunk * 16; }
+typedef __attribute__((address_space(3))) char lds_t;
 
 __device__ __forceinline__ int round_up(int n, int m) { return (n + m - 1) / m * m; }
 
@@ -62,15 +61,17 @@ __device__ __forceinline__ unsigned bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // ---------------------------------------------------------------------------
-// Global loads go through buffer resources: an offset past num_records
-// returns zeros, so tile edges (segment end, matrix edge) need no branches.
+// Global loads go through buffer resources: an offset past num_records reads
+// zero, so tile edges (segment end, matrix edge) need no branches.  The
+// descriptor must live in scalar registers; base and size are made provably
+// wave-uniform (readfirstlane) so the compiler never wraps a load in a
+// per-lane loop over descriptors.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr uint32_t kOob = 0x80000000u;   // any offset >= num_records reads 0
 
-// The descriptor must live in scalar registers; base and size are made
-// provably wave-uniform (readfirstlane) so the compiler never wraps a load in
-// a per-lane loop over descriptors.
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
   const uint32_t n = bytes > 0x7FFFFFFF ? 0x7FFFFFFFu : (uint32_t)bytes;
   const uint64_t p = (uint64_t)(uintptr_t)base;
@@ -80,112 +81,152 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(n),
                                            0x00020000);
 }
-__device__ __forceinline__ u32x4 bload(Rsrc r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+// 16 bytes per lane straight into LDS (LDS DMA): lane i lands at dst + 16 i.
+// Issued through inline assembly so the compiler does not track it: its
+// alias tracking cannot tell the four stage arrays apart and would insert a
+// wait for every load in flight before LDS reads of other stages.  Every
+// consumer is ordered explicitly instead (s_waitcnt vmcnt + barrier per
+// step).  The instruction writes no register; its operands are read at
+// issue; M0 carries the LDS base as an input operand.
+typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
+struct DmaRsrc {
+  u32x4s v;
+};
+__device__ __forceinline__ DmaRsrc make_dma_rsrc(const void* base, int64_t bytes) {
+  const uint32_t n = bytes > 0x7FFFFFFF ? 0x7FFFFFFFu : (uint32_t)bytes;
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  DmaRsrc r;
+  r.v[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  r.v[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xFFFFu);   // stride 0
+  r.v[2] = __builtin_amdgcn_readfirstlane(n);
+  r.v[3] = 0x00020000u;
+  return r;
+}
+__device__ __forceinline__ void load_lds(const DmaRsrc& r, lds_t* dst, uint32_t voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r.v), "{m0}"(m0)
+               : "memory");
 }
 // Stores past num_records are dropped: the epilogues need no branches.
 __device__ __forceinline__ void bstore16(Rsrc r, uint32_t voff, unsigned v) {
   __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, voff, 0, 0);
 }
 
-// Loader for an operand whose contraction index is contiguous: 256 tile rows
-// x 64 k.  Thread t covers chunk t%8 (8 k) of rows t/8 + 32 i.
-struct DirectTile {
-  static constexpr int kCommitValu = 0;   // VALU per LDS write in commit()
-  Rsrc rs;
-  uint32_t voff[8];
-  u32x4 v[8];
+// ---------------------------------------------------------------------------
+// Operand tiles in LDS (one per stage and operand, 16 KiB each).
+//
+// Row tile (operand contiguous along k): 256 rows x 32 k, rows of 64 B; the
+// 16-byte chunk c of row r sits at chunk c ^ ((r >> 2) & 3), so the 16 rows
+// read by a 16-lane group of an MFMA fragment load hit 16 distinct bank
+// groups.  One LDS-DMA load (a wave, 1 KiB) fills 16 rows.
+//
+// Column tile (operand stored [k][n], n contiguous): two regions of 128
+// columns (gate and up weights, or two column halves of one matrix), 32 k
+// rows of 256 B each; chunk c of row k sits at chunk c ^ (4 (k & 3)).  One
+// LDS-DMA load fills 4 rows of one region.  Fragments are read with the
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): lane q of a 16-lane
+// group points at row k0 + q/4, columns n0 + 4 (q%4) .. +3, and lane i then
+// holds column n0 + i, rows k0 .. k0+3 -- the MFMA operand layout.
+struct RowTile {
+  static constexpr bool kRows = true;
+  DmaRsrc rs;
+  uint32_t voff[4];
   // base: row 0, k 0 of the tile; ld: row stride (elements)
   __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int rows_valid) {
-    const int t = threadIdx.x, c = t & 7;
-    rs = make_rsrc(base, (int64_t)rows_valid * ld * 2);
+    const int w = wave_id(), lane = threadIdx.x & 63;
+    rs = make_dma_rsrc(base, (int64_t)rows_valid * ld * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (t >> 3) + 32 * i;
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * (w * 4 + i) + (lane >> 2);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
       voff[i] = r < rows_valid ? (uint32_t)(r * ld * 2 + c * 16) : kOob;
     }
   }
-  // the whole offset goes in the VGPR operand: the hardware range check
-  // covers that operand, not the scalar offset
-  __device__ __forceinline__ void issue(int64_t k0) {
+  __device__ __forceinline__ void issue(lds_t* tile, int64_t k0, bool valid) {
+    const int w = wave_id();
     const uint32_t ko = (uint32_t)(k0 * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = bload(rs, voff[i] + ko, 0);
+    for (int i = 0; i < 4; ++i)
+      load_lds(rs, tile + (w * 4 + i) * 1024, valid ? voff[i] + ko : kOob);
   }
-  __device__ __forceinline__ void commit(char* tile) const {
-    const int t = threadIdx.x, c = t & 7;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *(u32x4*)(tile + lds_off((t >> 3) + 32 * i, c)) = v[i];
+  // 8 consecutive k (sub-step kk, lane half lh) of tile row `row`
+  __device__ __forceinline__ static bf16x8 frag(const lds_t* tile, int row, int kk, int lh) {
+    const int c = (2 * kk + lh) ^ ((row >> 2) & 3);
+    return *(const __attribute__((address_space(3))) bf16x8*)(tile + row * 64 + c * 16);
   }
 };
 
-// Loader for an operand stored [k][n] (n contiguous): 64 k x 256 tile rows
-// (n).  Threads 0-127 fill tile rows [0,128) from src0, threads 128-255 rows
-// [128,256) from src1 (the gate and the up weights side by side, or two
-// column halves of one matrix), so every wave reads one matrix.  Thread t
-// covers k-block t%8 (8 k) and n-chunk (t/8)%16 (8 n); the 8x8 block is
-// transposed in registers so that each tile row holds 8 consecutive k.  With
-// k-blocks varying fastest, each 16-lane group of a transposed LDS write
-// covers 16 different bank groups.
-struct TransTile {
-  static constexpr int kCommitValu = 2;   // v_perm per LDS write (4 per 8, 2 loaders)
-  Rsrc rs;
-  uint32_t voff[8];
+struct ColTile {
+  static constexpr bool kRows = false;
+  DmaRsrc rs0, rs1;
+  uint32_t voff[4];
   uint32_t ld2;
-  u32x4 v[8];
-  // src0/src1: k 0, n 0 of each half; ld: k stride (elements); k_total: valid
-  // k rows from k 0; nv0/nv1: valid columns of each half
+  // src0/src1: k 0, n 0 of the two 128-column regions; ld: k stride
+  // (elements); k_total: valid k rows from k 0; nv0/nv1: valid columns
   __device__ __forceinline__ void init(const uint16_t* src0, const uint16_t* src1, int64_t ld,
                                        int64_t k_total, int nv0, int nv1) {
-    const int t = threadIdx.x, half = t >> 7;
-    const int kb = t & 7, n = ((t >> 3) & 15) * 8;
-    const uint16_t* src = half ? src1 : src0;
-    const int nv = half ? nv1 : nv0;
-    rs = make_rsrc(src, k_total * ld * 2);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = kb * 8 + i;
-      voff[i] = n < nv ? (uint32_t)(k * ld * 2 + n * 2) : kOob;
-    }
+    const int w = wave_id(), lane = threadIdx.x & 63;
+    rs0 = make_dma_rsrc(src0, k_total * ld * 2);
+    rs1 = make_dma_rsrc(src1, k_total * ld * 2);
     ld2 = (uint32_t)(ld * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = w * 4 + i;                       // region b >> 3
+      const int k = 4 * (b & 7) + (lane >> 4);
+      const int col = 8 * ((lane & 15) ^ (4 * (k & 3)));
+      const int nv = (b >> 3) ? nv1 : nv0;
+      voff[i] = col < nv ? (uint32_t)(k * ld * 2 + col * 2) : kOob;
+    }
   }
-  __device__ __forceinline__ void issue(int64_t k0) {
+  __device__ __forceinline__ void issue(lds_t* tile, int64_t k0, bool valid) {
+    const int w = wave_id();
     const uint32_t ko = (uint32_t)(k0 * ld2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = bload(rs, voff[i] + ko, 0);
-  }
-  __device__ __forceinline__ void commit(char* tile) const {
-    const int t = threadIdx.x, half = t >> 7;
-    const int kb = t & 7, c = (t >> 3) & 15;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int sel = (j & 1) ? 0x07060302 : 0x05040100;
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o[q] = __builtin_amdgcn_perm(v[2 * q + 1][j >> 1], v[2 * q][j >> 1], sel);
-      *(u32x4*)(tile + lds_off(half * 128 + c * 8 + j, kb)) = o;
+    for (int i = 0; i < 4; ++i) {
+      const int b = w * 4 + i;
+      load_lds((b >> 3) ? rs1 : rs0, tile + b * 1024, valid ? voff[i] + ko : kOob);
     }
+  }
+  // 8 consecutive k (sub-step kk, lane half lh) of tile column n (the lane's)
+  __device__ __forceinline__ static bf16x8 frag(const lds_t* tile, int nb, int kk, int lh) {
+    const int lane = threadIdx.x & 63, q = lane & 15, g = (lane >> 4) & 1;
+    const lds_t* region = tile + (nb >> 7) * 8192;
+    const int col = (nb & 127) + 16 * g + 4 * (q & 3);
+    i16x4 h[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int k = 16 * kk + 8 * lh + 4 * hh + (q >> 2);
+      const int off = k * 256 + (((col >> 3) ^ (4 * (k & 3))) << 4) + (col & 7) * 2;
+      h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(region + off));
+    }
+    const i16x8 v = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
   }
 };
 
 // MFMA fragments of one 16-deep sub-step for a wave: A rows arow0 + 32 i,
-// B^T rows nrow[j] (+ lane%32), k-chunk 2 kk + lane/32.
+// B columns nrow[j] (+ lane%32).
 struct Frags {
   bf16x8 a[4], b[4];
 };
 
-__device__ __forceinline__ void read_frags(Frags& f, const char* stage, int kk, int arow0,
+template <class TA, class TB>
+__device__ __forceinline__ void read_frags(Frags& f, const lds_t* stage, int kk, int arow0,
                                            const int nrow[4]) {
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
-  const char* A = stage;
-  const char* Bt = stage + kTileBytes;
+  const lds_t* A = stage;
+  const lds_t* Bt = stage + kTileBytes;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    f.a[i] = *(const bf16x8*)(A + lds_off(arow0 + i * 32 + lr, 2 * kk + lh));
+    f.a[i] = TA::kRows ? RowTile::frag(A, arow0 + i * 32 + lr, kk, lh)
+                       : ColTile::frag(A, arow0 + i * 32, kk, lh);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    f.b[j] = *(const bf16x8*)(Bt + lds_off(nrow[j] + lr, 2 * kk + lh));
+    f.b[j] = TB::kRows ? RowTile::frag(Bt, nrow[j] + lr, kk, lh)
+                       : ColTile::frag(Bt, nrow[j], kk, lh);
 }
 
 __device__ __forceinline__ void mma16(f32x16 acc[4][4], const Frags& f) {
@@ -196,77 +237,90 @@ __device__ __forceinline__ void mma16(f32x16 acc[4][4], const Frags& f) {
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-// Scheduling groups (LLVM AMDGPU sched_group_barrier masks).
-constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100, kSgDsWrite = 0x200;
+// Wait until at most N LDS-DMA loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else static_assert(N == 0, "unsupported count");
+}
+
+constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
 #define MOONEP_SG(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
-// One sub-step: 8 fragment reads for the next sub-step, then 16 MFMAs on the
-// current fragments (the reads' latency hides behind the MFMAs).
-#define MOONEP_SUBSTEP()      \
-  do {                        \
-    MOONEP_SG(kSgDsRead, 8);  \
-    MOONEP_SG(kSgMfma, 16);   \
-    __builtin_amdgcn_sched_barrier(0); \
-  } while (0)
+// The four LDS stages are four separate arrays and the K loop is unrolled by
+// four, so every LDS access names its stage statically: the compiler can
+// then see that a fragment read never aliases an LDS-DMA load still in
+// flight into another stage and inserts no wait for it.
+struct Stages {
+  lds_t* p[kStages];
+};
 
-// The K loop shared by every GEMM here.  Two LDS stages; per 64-deep step:
-// the next step's global loads are issued first; sub-steps 0-2 each read the
-// following sub-step's fragments while 16 MFMAs run; during sub-step 2 the
-// loaded tiles are transposed / written to the other stage, interleaved one
-// LDS write per MFMA; one barrier; sub-step 3's MFMAs cover the read of the
-// next step's first fragments.  Scheduling barriers pin this order (left
-// alone, the compiler sinks the loads next to their consumers and exposes the
-// memory latency).  The last step is peeled.
+#define MOONEP_STAGE_ARRAYS(name)                                           \
+  __shared__ __attribute__((aligned(16))) char name##0_[kStageBytes];      \
+  __shared__ __attribute__((aligned(16))) char name##1_[kStageBytes];      \
+  __shared__ __attribute__((aligned(16))) char name##2_[kStageBytes];      \
+  __shared__ __attribute__((aligned(16))) char name##3_[kStageBytes];      \
+  const Stages name = {{(lds_t*)name##0_, (lds_t*)name##1_, (lds_t*)name##2_, (lds_t*)name##3_}}
+
+// One 32-deep step kt, held in stage S = kt % 4: sub-step 0 reads sub-step
+// 1's fragments while 16 MFMAs run; wait for the next step's loads, one
+// barrier, issue the loads of step kt+3 into stage (S+3)%4 (retired by the
+// barrier); sub-step 1 reads the next step's first fragments while its 16
+// MFMAs run.  Loads past the last step read nothing (out-of-range offset), so
+// the wait counts stay fixed.
+template <int S, class TA, class TB>
+__device__ __forceinline__ void kstep(TA& la, TB& lb, const Stages& st, int kt, int nk,
+                                      Frags& f0, Frags& f1, f32x16 acc[4][4], int arow0,
+                                      const int nrow[4]) {
+  constexpr int N = (S + 1) % kStages, L = (S + kStages - 1) % kStages;
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<TA, TB>(f1, st.p[S], 1, arow0, nrow);
+  mma16(acc, f0);
+  MOONEP_SG(kSgDsRead, 16);
+  MOONEP_SG(kSgMfma, 16);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_loads<kLoadsPerStep>();
+  __syncthreads();
+  const int nx = kt + kStages - 1;
+  la.issue(st.p[L], (int64_t)nx * BK, nx < nk);
+  lb.issue(st.p[L] + kTileBytes, (int64_t)nx * BK, nx < nk);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<TA, TB>(f0, st.p[N], 0, arow0, nrow);
+  mma16(acc, f1);
+  MOONEP_SG(kSgDsRead, 16);
+  MOONEP_SG(kSgMfma, 16);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The K loop shared by every GEMM here: a ring of 4 LDS stages filled by
+// LDS-DMA loads issued 3 steps ahead (no staging registers, no LDS write
+// instructions), one barrier per step.
 template <class TA, class TB>
-__device__ __forceinline__ void gemm_loop(TA& la, TB& lb, char* smem, int nk, f32x16 acc[4][4],
-                                          int arow0, const int nrow[4]) {
+__device__ __forceinline__ void gemm_loop(TA& la, TB& lb, const Stages& st, int nk,
+                                          f32x16 acc[4][4], int arow0, const int nrow[4]) {
   if (nk <= 0) return;
-  la.issue(0);
-  lb.issue(0);
-  la.commit(smem);
-  lb.commit(smem + kTileBytes);
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) {
+    la.issue(st.p[s], (int64_t)s * BK, s < nk);
+    lb.issue(st.p[s] + kTileBytes, (int64_t)s * BK, s < nk);
+  }
+  wait_loads<2 * kLoadsPerStep>();
   __syncthreads();
   Frags f0, f1;
-  read_frags(f0, smem, 0, arow0, nrow);
+  read_frags<TA, TB>(f0, st.p[0], 0, arow0, nrow);
   int kt = 0;
-  for (; kt + 1 < nk; ++kt) {
-    char* cur = smem + (kt & 1) * kStageBytes;
-    char* nxt = smem + ((kt + 1) & 1) * kStageBytes;
-    __builtin_amdgcn_sched_barrier(0);
-    la.issue((int64_t)(kt + 1) * BK);
-    lb.issue((int64_t)(kt + 1) * BK);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(f1, cur, 1, arow0, nrow);
-    mma16(acc, f0);
-    MOONEP_SUBSTEP();
-    read_frags(f0, cur, 2, arow0, nrow);
-    mma16(acc, f1);
-    MOONEP_SUBSTEP();
-    read_frags(f1, cur, 3, arow0, nrow);
-    mma16(acc, f0);
-    la.commit(nxt);
-    lb.commit(nxt + kTileBytes);
-    MOONEP_SG(kSgDsRead, 8);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      MOONEP_SG(kSgValu, TA::kCommitValu + TB::kCommitValu);
-      MOONEP_SG(kSgDsWrite, 1);
-      MOONEP_SG(kSgMfma, 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    read_frags(f0, nxt, 0, arow0, nrow);
-    mma16(acc, f1);
-    MOONEP_SUBSTEP();
+  for (; kt + kStages <= nk; kt += kStages) {
+    kstep<0>(la, lb, st, kt + 0, nk, f0, f1, acc, arow0, nrow);
+    kstep<1>(la, lb, st, kt + 1, nk, f0, f1, acc, arow0, nrow);
+    kstep<2>(la, lb, st, kt + 2, nk, f0, f1, acc, arow0, nrow);
+    kstep<3>(la, lb, st, kt + 3, nk, f0, f1, acc, arow0, nrow);
   }
-  char* cur = smem + (kt & 1) * kStageBytes;
-  read_frags(f1, cur, 1, arow0, nrow);
-  mma16(acc, f0);
-  read_frags(f0, cur, 2, arow0, nrow);
-  mma16(acc, f1);
-  read_frags(f1, cur, 3, arow0, nrow);
-  mma16(acc, f0);
-  mma16(acc, f1);
+  if (kt < nk) kstep<0>(la, lb, st, kt, nk, f0, f1, acc, arow0, nrow);
+  if (kt + 1 < nk) kstep<1>(la, lb, st, kt + 1, nk, f0, f1, acc, arow0, nrow);
+  if (kt + 2 < nk) kstep<2>(la, lb, st, kt + 2, nk, f0, f1, acc, arow0, nrow);
+  wait_loads<0>();
 }
 
 __device__ __forceinline__ void zero_acc(f32x16 acc[4][4]) {
@@ -362,7 +416,7 @@ __global__ void gemm_schedule(const int32_t* act, const int32_t* cu, const int32
 // ---------------------------------------------------------------------------
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1))) void ffn_gateup(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  MOONEP_STAGE_ARRAYS(smem);
   int d, nt;
   Tile tl;
   if (!decode(a, &d, &tl, &nt)) return;
@@ -372,8 +426,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int nrow[4] = {wn * 64, wn * 64 + 32, 128 + wn * 64, 128 + wn * 64 + 32};
 
-  DirectTile la;
-  TransTile lb;
+  RowTile la;
+  ColTile lb;
   la.init(a.x + ((int64_t)d * a.NvS + tl.m0) * a.H, a.H, rows_valid);
   lb.init(weight_row(a, 0, d, tl.row) + n0, weight_row(a, 1, d, tl.row) + n0, a.Hp, a.H, nvh,
           nvh);
@@ -406,7 +460,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 // ---------------------------------------------------------------------------
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1))) void ffn_down(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  MOONEP_STAGE_ARRAYS(smem);
   int d, nt;
   Tile tl;
   if (!decode(a, &d, &tl, &nt)) return;
@@ -416,7 +470,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int nrow[4] = {wn * 128, wn * 128 + 32, wn * 128 + 64, wn * 128 + 96};
 
-  DirectTile la, lb;
+  RowTile la, lb;
   la.init(a.z + ((int64_t)d * a.NvS + tl.m0) * a.Hp, a.Hp, rows_valid);
   lb.init(weight_row(a, 2, d, tl.row) + (int64_t)n0 * a.Hp, a.Hp, cols_valid);
   f32x16 acc[4][4];
@@ -456,7 +510,7 @@ struct WgradArgs {
 // Tile: 256 h (MFMA rows) x 256 h' (MFMA columns), contraction over t.
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1))) void wgrad_kernel(WgradArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  MOONEP_STAGE_ARRAYS(smem);
   const int64_t lt = logical_tile();
   const int64_t total = (int64_t)a.nranks * a.L2 * a.ntm * a.ntn;
   if (lt >= total) return;
@@ -479,7 +533,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int nrow[4] = {wn * 128, wn * 128 + 32, wn * 128 + 64, wn * 128 + 96};
 
-  TransTile la, lb;
+  ColTile la, lb;
   la.init(A, A + 128, a.H, ntok, mv0, mv1);
   lb.init(Bm, Bm + 128, a.Hp, ntok, nv0, nv1);
   f32x16 acc[4][4];
