@@ -391,26 +391,50 @@ __device__ __forceinline__ bool decode(const FfnArgs& a, int* d, Tile* tl, int* 
 }
 
 // ---------------------------------------------------------------------------
-__global__ void gemm_schedule(const int32_t* act, const int32_t* cu, const int32_t* segn,
-                              int32_t* tiles, int32_t* ntiles, int L2, int EB, int tp,
-                              int max_tiles) {
-  if (threadIdx.x != 0) return;
-  const int d = blockIdx.x;
-  int t = 0;
-  for (int q = 0; q < L2; ++q) {
-    const int row = act[d * L2 + q];
-    if (row < 0) break;
-    const int end = cu[d * EB + row];
-    const int len = round_up(segn[d * EB + row], tp);
-    for (int m = end - len; m < end && t < max_tiles; m += BM, ++t) {
+// One workgroup of 256 threads per rank: thread q takes active row q, counts
+// its M-tiles, a block-wide exclusive scan places them, and the thread writes
+// its tiles.
+__global__ __launch_bounds__(256) void gemm_schedule(const int32_t* act, const int32_t* cu,
+                                                     const int32_t* segn, int32_t* tiles,
+                                                     int32_t* ntiles, int L2, int EB, int tp,
+                                                     int max_tiles) {
+  __shared__ int wsum[4];
+  __shared__ int s_total;
+  const int d = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int base = 0;
+  for (int q0 = 0; q0 < L2; q0 += 256) {
+    const int q = q0 + tid;
+    const int row = q < L2 ? act[d * L2 + q] : -1;
+    int end = 0, len = 0, n = 0;
+    if (row >= 0) {
+      end = cu[d * EB + row];
+      len = round_up(segn[d * EB + row], tp);
+      n = (len + BM - 1) / BM;
+    }
+    int x = n;                                   // inclusive scan within the wave
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    int before = 0;
+    for (int i = 0; i < wv; ++i) before += wsum[i];
+    if (tid == 255) s_total = before + x;
+    int t = base + before + x - n;
+    for (int m = end - len; m < end; m += BM, ++t) {
+      if (t >= max_tiles) break;
       int32_t* e = tiles + ((int64_t)d * max_tiles + t) * 4;
       e[0] = row;
       e[1] = m;
       e[2] = m + BM < end ? m + BM : end;
       e[3] = 0;
     }
+    __syncthreads();
+    base += s_total;
+    __syncthreads();
   }
-  ntiles[d] = t;
+  if (tid == 0) ntiles[d] = base < max_tiles ? base : max_tiles;
 }
 
 // ---------------------------------------------------------------------------
@@ -571,7 +595,7 @@ hipError_t launch_ffn(const Ctx& c, const moonep_plan_t& p, int rank, const uint
                       const uint16_t* const home[3], const uint16_t* const pool[3], uint16_t* z,
                       uint16_t* y, hipStream_t s) {
   const Dims& d = c.d;
-  gemm_schedule<<<d.R, 64, 0, s>>>(p.aux + d.aux.act, p.cu_seqlens, p.seg_tokens, c.tiles,
+  gemm_schedule<<<d.R, 256, 0, s>>>(p.aux + d.aux.act, p.cu_seqlens, p.seg_tokens, c.tiles,
                                    c.ntiles, 2 * d.L, d.E + d.B, d.tp, c.max_tiles);
   FfnArgs a;
   a.x = x_nvs;

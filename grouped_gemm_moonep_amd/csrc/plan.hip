@@ -149,14 +149,21 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   __syncthreads();
 
   // Phase A: counts per (r, e) and exclusive per-chunk prefix (in place).
+  // Loads are batched 8 at a time so each thread keeps 8 in flight.
   for (int idx = tid; idx < RE; idx += kSolveThreads) {
     const int r = idx / E, e = idx - (idx / E) * E;
     int32_t* col = a.cc + (int64_t)r * nch * E + e;
     int run = 0;
-    for (int ch = 0; ch < nch; ++ch) {
-      const int v = col[(int64_t)ch * E];
-      col[(int64_t)ch * E] = run;
-      run += v;
+    for (int ch0 = 0; ch0 < nch; ch0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = ch0 + u < nch ? col[(int64_t)(ch0 + u) * E] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (ch0 + u < nch) {
+          col[(int64_t)(ch0 + u) * E] = run;
+          run += v[u];
+        }
     }
     a.counts[idx] = run;
     if (a.tpe && a.tpe[idx] != run) atomicOr(&s_err, MOONEP_ROUTE_COUNTS);
@@ -170,10 +177,16 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   // Phase B: expert loads T_e and the exclusive prefix over ranks.
   for (int e = tid; e < E; e += kSolveThreads) {
     int run = 0;
-    for (int r = 0; r < R; ++r) {
-      const int v = a.counts[r * E + e];
-      a.rankpre[r * E + e] = run;
-      run += v;
+    for (int r0 = 0; r0 < R; r0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = r0 + u < R ? a.counts[(r0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (r0 + u < R) {
+          a.rankpre[(r0 + u) * E + e] = run;
+          run += v[u];
+        }
     }
     T[e] = run;
     atomicMax(&s_maxload, run);
@@ -451,10 +464,23 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
 
   // Phase H: per-chunk line bases for plan_assign.
   const int64_t ncc = (int64_t)R * nch * E;
-  for (int64_t idx = tid; idx < ncc; idx += kSolveThreads) {
-    const int e = (int)(idx % E);
-    const int r = (int)(idx / ((int64_t)nch * E));
-    a.cc[idx] += aline[e] + a.rankpre[r * E + e];
+  for (int64_t i0 = tid; i0 < ncc; i0 += 8 * kSolveThreads) {
+    int v[8], w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t idx = i0 + (int64_t)u * kSolveThreads;
+      if (idx < ncc) {
+        const int e = (int)(idx % E);
+        const int r = (int)(idx / ((int64_t)nch * E));
+        v[u] = a.cc[idx];
+        w[u] = aline[e] + a.rankpre[r * E + e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t idx = i0 + (int64_t)u * kSolveThreads;
+      if (idx < ncc) a.cc[idx] = v[u] + w[u];
+    }
   }
 
   if (tid == 0) {
@@ -473,30 +499,46 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
 
 // ---------------------------------------------------------------------------
 // plan_assign: one workgroup per (chunk, rank).
+constexpr int kShiftLds = 4096;     // shift table staged in LDS up to R*E ints
+constexpr int kPiecesLds = 1024;    // piece table staged in LDS up to this many ints
+
 __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
   __shared__ unsigned long long mask[4][kMaxE];
+  __shared__ int s_base[kMaxE];
+  __shared__ int s_shift[kShiftLds];
+  __shared__ int s_pieces[kPiecesLds];
+  __shared__ int s_np[kMaxR];
   const int ch = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
   const int err = a.stats[MOONEP_STAT_ERROR];
   const int s = ch * kPlanChunk + tid;
   const int w = tid >> 6, lane = tid & 63;
   const unsigned long long bit = 1ull << lane;
   const int64_t tok = (int64_t)r * a.S + s;
+  // the lookup tables of this chunk, staged in LDS when they fit
+  const int npc = a.R * (a.R + 1) * 2;
+  const bool tab = a.R * a.E <= kShiftLds && npc <= kPiecesLds;
   if (!err) {
     for (int i = tid; i < 4 * a.E; i += kPlanChunk) mask[i / a.E][i % a.E] = 0ull;
+    const int32_t* gbase = a.cc + ((int64_t)r * a.nch + ch) * a.E;
+    for (int i = tid; i < a.E; i += kPlanChunk) s_base[i] = gbase[i];
+    for (int i = tid; i < a.R; i += kPlanChunk) s_np[i] = a.npieces[i];
+    if (tab) {
+      for (int i = tid; i < a.R * a.E; i += kPlanChunk) s_shift[i] = a.shift[i];
+      for (int i = tid; i < npc; i += kPlanChunk) s_pieces[i] = a.pieces[i];
+    }
     __syncthreads();
     if (s < a.S)
       for (int k = 0; k < a.K; ++k) atomicOr(&mask[w][a.topk[tok * a.K + k]], bit);
     __syncthreads();
     if (s < a.S) {
-      const int32_t* base = a.cc + ((int64_t)r * a.nch + ch) * a.E;
       for (int k = 0; k < a.K; ++k) {
         const int e = a.topk[tok * a.K + k];
         int below = __popcll(mask[w][e] & (bit - 1));
         for (int v = 0; v < w; ++v) below += __popcll(mask[v][e]);
-        const int pos = base[e] + below;
+        const int pos = s_base[e] + below;
         const int g = e / a.L;
-        const int32_t* pg = a.pieces + (int64_t)g * (a.R + 1) * 2;
-        const int np = a.npieces[g];
+        const int32_t* pg = (tab ? (const int32_t*)s_pieces : a.pieces) + (int64_t)g * (a.R + 1) * 2;
+        const int np = s_np[g];
         int d = pg[1];
         for (int p = 0; p < np; ++p) {
           if (pos < pg[2 * p]) { d = pg[2 * p + 1]; break; }
@@ -506,7 +548,7 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
           a.dest[id] = r * a.NvS + s * a.K + k;
           continue;
         }
-        const int slot = a.shift[d * a.E + e] + pos;
+        const int slot = (tab ? s_shift[d * a.E + e] : a.shift[d * a.E + e]) + pos;
         if ((unsigned)slot >= (unsigned)a.NvS) {  // cannot happen for a valid plan
           a.dest[id] = r * a.NvS + s * a.K + k;
           continue;
