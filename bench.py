@@ -44,7 +44,36 @@ def alg_bytes(w):
 
 
 def ffn_flops(w):
+    """Algorithmic flops of the grouped FFN over every real slot (padding rows
+    not counted): gate and up 2*H*H' each, down 2*H*H' per slot."""
     return 6.0 * w.H * w.Hp * w.R * w.S * w.K
+
+
+def gateup_flops(w):
+    return 4.0 * w.H * w.Hp * w.R * w.S * w.K
+
+
+def down_flops(w):
+    return 2.0 * w.H * w.Hp * w.R * w.S * w.K
+
+
+TRAFFIC_FILE = os.path.join(REPO, "profiles", "traffic_ffn_gateup_fwd_r8_s4096_k8_e256.txt")
+KERNEL_SOURCE = os.path.join(REPO, "grouped_gemm_moonep_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic():
+    """HBM bytes per ffn_gateup launch from the committed counter summary, or
+    None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE)
+                      if ":" in line and not line.startswith(" "))
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if fields.get("source_sha256", "").strip() != src:
+        return None
+    return int(fields["hbm_bytes_per_launch"].strip())
 
 
 def cpu_baseline(w, topk, rw, width=512):
@@ -78,6 +107,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--targets", default="0,0.5,1,2,4,adv")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="before warmup, run torch.neg over a float32 buffer of MIB MiB "
+                         "three times: a plain kernel of known traffic (reads and writes "
+                         "MIB MiB) that calibrates FETCH_SIZE / WRITE_SIZE counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the R EP ranks are emulated as R regions "
@@ -125,11 +158,23 @@ def main():
         rec(2)
         buf.prefetch_weight(plan, home, pool)
         rec(3)
-        buf.expert_ffn(plan, x_nvs, home, pool, z_ws, x_nvs)      # in place (zero copy)
+        buf.expert_gateup(plan, x_nvs, home, pool, z_ws)
         rec(4)
-        buf.combine(plan, x_nvs, rw_nvs, out=out, rw_sk=rw_sk)
+        buf.expert_down(plan, z_ws, home, pool, x_nvs)      # in place (zero copy)
         rec(5)
+        buf.combine(plan, x_nvs, rw_nvs, out=out, rw_sk=rw_sk)
+        rec(6)
         return t
+
+    if args.copy_probe > 0:
+        n = args.copy_probe * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
+        print(f"[bench] copy probe: 3 x neg over {args.copy_probe} MiB", file=sys.stderr, flush=True)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -144,7 +189,7 @@ def main():
         stats[t] = {"dups": int(st[1]), "maxvio": float(np.int32(st[5]).view(np.float32)),
                     "pad_rows": int(st[4])}
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -154,16 +199,19 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    names = ["plan", "dispatch", "prefetch", "ffn", "combine"]
+    names = ["plan", "dispatch", "prefetch", "gateup", "down", "combine"]
     per = {n: [] for n in names}
     for ev in events:
         for j, n in enumerate(names):
             per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)     # seconds
+    per["ffn"] = [a + b for a, b in zip(per["gateup"], per["down"])]
     pb, db, cb = alg_bytes(w)
     t_pdc = sum(per["plan"]) + sum(per["dispatch"]) + sum(per["combine"])
     gbs = args.steps * (pb + db + cb) / t_pdc / 1e9
     t_ffn = float(np.mean(per["ffn"]))
     tflops = ffn_flops(w) / t_ffn / 1e12
+    t_gu = float(np.mean(per["gateup"]))
+    t_dn = float(np.mean(per["down"]))
     t_disp = float(np.mean(per["dispatch"]))
     t_comb = float(np.mean(per["combine"]))
 
@@ -178,6 +226,7 @@ def main():
             "pad_rows": stats[t]["pad_rows"],
             "plan_us": round(m("plan") * 1e6, 2), "dispatch_us": round(m("dispatch") * 1e6, 1),
             "prefetch_us": round(m("prefetch") * 1e6, 1), "ffn_ms": round(m("ffn") * 1e3, 3),
+            "gateup_ms": round(m("gateup") * 1e3, 3), "down_ms": round(m("down") * 1e3, 3),
             "combine_us": round(m("combine") * 1e6, 1),
             "pdc_GBps": round((pb + db + cb) / (m("plan") + m("dispatch") + m("combine")) / 1e9, 1),
             "gemm_TFLOPs": round(ffn_flops(w) / m("ffn") / 1e12, 1),
@@ -192,13 +241,19 @@ def main():
         "config": {"workload": WORKLOAD, "R": w.R, "S": w.S, "K": w.K, "E": w.E, "B": w.B,
                    "H": w.H, "Hp": w.Hp, "token_padding": w.token_padding,
                    "maxvio_targets": [str(t) for t in targets],
-                   "step": "plan, dispatch, prefetch_weight, grouped SwiGLU FFN (8 ranks), combine"},
+                   "step": "plan, dispatch, prefetch_weight, expert_gateup + expert_down (8 ranks), combine"},
         "gemm_tflops": round(tflops, 1),
-        "roofline": {"kernel": "grouped SwiGLU FFN (ffn_gateup + ffn_down, one call, 8 ranks)",
-                     "bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None,
-                     "per_launch": {"flops": ffn_flops(w), "avg_s": t_ffn}},
+        "roofline": {"kernel": "ffn_gateup (gate and up GEMMs + SwiGLU, all 8 ranks, one launch)",
+                     "bound": "mfma", "achieved": round(gateup_flops(w) / t_gu / 1e12, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gateup_flops(w) / t_gu / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(),
+                     "per_launch": {"flops": gateup_flops(w), "avg_s": t_gu}},
+        "roofline_down": {"kernel": "ffn_down (down GEMM, all 8 ranks, one launch)",
+                          "bound": "mfma", "achieved": round(down_flops(w) / t_dn / 1e12, 1),
+                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(down_flops(w) / t_dn / 1e12 / BF16_PEAK_TFLOPS, 4),
+                          "traffic": None, "per_launch": {"flops": down_flops(w), "avg_s": t_dn}},
         "roofline_dispatch": {"bound": "hbm", "achieved": round(db / t_disp / 1e9, 1),
                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(db / t_disp / 1e9 / HBM_PEAK_GBS, 4),

@@ -10,6 +10,7 @@ device memory and the current stream; nothing is computed in Python.
     x_nvs, rw_nvs = buf.dispatch(plan, x, rw)       # moonep_dispatch
     buf.prefetch_weight(plan, home, pool)           # moonep_prefetch_weight
     buf.expert_ffn(plan, x_nvs, home, pool, z, y)   # moonep_expert_ffn
+                                                    # (= expert_gateup + expert_down)
     out, rw_sk = buf.combine(plan, y, rw_nvs)       # moonep_combine
 """
 from __future__ import annotations
@@ -139,13 +140,13 @@ class Buffer:
                    "moonep_combine")
         return out, rw_sk
 
-    def _weights(self, ts, pool):
+    def _weights(self, ts, pool, used=(0, 1, 2)):
         R, E, B, H, Hp = self.R, self.E, self.B, self.H, self.Hp
         if len(ts) != 3:
             raise ValueError("three projections (gate, up, down) expected")
         shape = (R, B, H, Hp) if pool else (E, H, Hp)
         for i, t in enumerate(ts):
-            if pool and B == 0 and t is None:
+            if t is None and (i not in used or (pool and B == 0)):
                 continue
             _dev_ptr(t, torch.bfloat16, shape, f"{'pool' if pool else 'home'}[{i}]")
         return _abi.ptr3(ts)
@@ -169,6 +170,28 @@ class Buffer:
         _abi.check(lib().moonep_expert_ffn(self._h, ctypes.byref(plan.struct), *args, _stream()),
                    "moonep_expert_ffn")
         return z_ws, y_nvs
+
+    def expert_gateup(self, plan, x_nvs, home, pool, z_nvs=None, rank=-1):
+        R, NvS, H, Hp = self.R, self.NvS, self.H, self.Hp
+        if z_nvs is None:
+            z_nvs = torch.empty((R, NvS, Hp), dtype=torch.bfloat16, device=x_nvs.device)
+        args = (int(rank), _dev_ptr(x_nvs, torch.bfloat16, (R, NvS, H), "x_nvs"),
+                self._weights(home, False, (0, 1)), self._weights(pool, True, (0, 1)),
+                _dev_ptr(z_nvs, torch.bfloat16, (R, NvS, Hp), "z_nvs"))
+        _abi.check(lib().moonep_expert_gateup(self._h, ctypes.byref(plan.struct), *args,
+                                              _stream()), "moonep_expert_gateup")
+        return z_nvs
+
+    def expert_down(self, plan, z_nvs, home, pool, y_nvs=None, rank=-1):
+        R, NvS, H, Hp = self.R, self.NvS, self.H, self.Hp
+        if y_nvs is None:
+            y_nvs = torch.empty((R, NvS, H), dtype=torch.bfloat16, device=z_nvs.device)
+        args = (int(rank), _dev_ptr(z_nvs, torch.bfloat16, (R, NvS, Hp), "z_nvs"),
+                self._weights(home, False, (2,)), self._weights(pool, True, (2,)),
+                _dev_ptr(y_nvs, torch.bfloat16, (R, NvS, H), "y_nvs"))
+        _abi.check(lib().moonep_expert_down(self._h, ctypes.byref(plan.struct), *args,
+                                            _stream()), "moonep_expert_down")
+        return y_nvs
 
     def expert_wgrad(self, plan, a_nvs, b_nvs, grad_home, reduce_buf, rank=-1):
         R, NvS, E, B, H, Hp = self.R, self.NvS, self.E, self.B, self.H, self.Hp

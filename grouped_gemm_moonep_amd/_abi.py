@@ -44,7 +44,7 @@ def lib():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m grouped_gemm_moonep_amd.build`")
+                          "`python grouped_gemm_moonep_amd/build.py`")
     try:
         import torch  # noqa: F401  (share torch's HIP runtime if it is loaded)
     except ImportError:
@@ -64,6 +64,8 @@ def lib():
         "moonep_combine": (i32, [vp, ctypes.POINTER(MoonepPlan), vp, i32, vp, vp, vp, vp]),
         "moonep_prefetch_weight": (i32, [vp, ctypes.POINTER(MoonepPlan), P3, P3, vp]),
         "moonep_expert_ffn": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, P3, P3, vp, vp, vp]),
+        "moonep_expert_gateup": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, P3, P3, vp, vp]),
+        "moonep_expert_down": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, P3, P3, vp, vp]),
         "moonep_expert_wgrad": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, vp, vp, vp, vp]),
         "moonep_reduce_grad": (i32, [vp, ctypes.POINTER(MoonepPlan), P3, P3, vp]),
         "moonep_read_stats": (i32, [vp, ctypes.POINTER(MoonepPlan), vp, vp]),

@@ -1,6 +1,6 @@
 """Build libmoonep.so for gfx950 with hipcc (in-tree).
 
-    python -m grouped_gemm_moonep_amd.build
+    python grouped_gemm_moonep_amd/build.py
 
 Every source under csrc/ is compiled for --offload-arch=gfx950 and linked
 into grouped_gemm_moonep_amd/libmoonep.so.  Packed-fp32 instructions are

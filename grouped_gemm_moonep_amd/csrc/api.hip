@@ -45,7 +45,10 @@ bool dims_from_config(const moonep_config_t* cfg, Dims* out) {
   a.dup_first = a.dup_e + RB;
   a.dup_cnt = a.dup_first + RB;
   a.hold = a.dup_cnt + RB;
-  a.total = a.hold + RB;
+  d.max_tiles = (int)(ceil_div(d.NvS, kGemmTileM) + 2 * d.L);
+  a.tiles = a.hold + RB;
+  a.ntiles = a.tiles + 4LL * c.R * d.max_tiles;
+  a.total = a.ntiles + c.R;
   *out = d;
   return true;
 }
@@ -126,7 +129,6 @@ moonep_status_t moonep_create(const moonep_config_t* cfg, moonep_handle_t* out) 
     free(h);
     return MOONEP_ERR_HIP;
   }
-  c.max_tiles = (int)(ceil_div(d.NvS, kGemmTileM) + 2 * d.L);
   struct { int32_t** p; int64_t n; } allocs[] = {
       {&c.cc, (int64_t)d.R * d.nch * d.E},
       {&c.rankpre, (int64_t)d.R * d.E},
@@ -135,8 +137,6 @@ moonep_status_t moonep_create(const moonep_config_t* cfg, moonep_handle_t* out) 
       {&c.npieces, d.R},
       {&c.line, d.E},
       {&c.chunk_err, (int64_t)d.R * d.nch},
-      {&c.tiles, (int64_t)d.R * c.max_tiles * 4},
-      {&c.ntiles, d.R},
   };
   for (auto& a : allocs) {
     if (hipMalloc((void**)a.p, (size_t)a.n * sizeof(int32_t)) != hipSuccess) {
@@ -152,7 +152,7 @@ moonep_status_t moonep_destroy(moonep_handle_t h) {
   if (!h) return MOONEP_OK;
   Ctx& c = h->c;
   int32_t* ptrs[] = {c.cc, c.rankpre, c.shift, c.pieces, c.npieces, c.line,
-                     c.chunk_err, c.tiles, c.ntiles};
+                     c.chunk_err};
   hipError_t err = hipSuccess;
   for (int32_t* p : ptrs)
     if (p) {
@@ -168,7 +168,9 @@ moonep_status_t moonep_plan(moonep_handle_t h, const int32_t* topk,
                             const moonep_plan_t* plan, hipStream_t stream) {
   if (!h || !topk || !aligned(topk, 4) || !plan_ok(plan)) return MOONEP_ERR_ARG;
   if (tokens_per_expert && !aligned(tokens_per_expert, 4)) return MOONEP_ERR_ARG;
-  return hip_status(launch_plan(h->c, topk, tokens_per_expert, *plan, stream));
+  hipError_t e = launch_plan(h->c, topk, tokens_per_expert, *plan, stream);
+  if (e == hipSuccess) e = launch_gemm_schedule(h->c, *plan, stream);
+  return hip_status(e);
 }
 
 moonep_status_t moonep_dispatch(moonep_handle_t h, const moonep_plan_t* plan,
@@ -205,21 +207,55 @@ moonep_status_t moonep_prefetch_weight(moonep_handle_t h, const moonep_plan_t* p
   return hip_status(launch_prefetch(h->c, *plan, home, pool, stream));
 }
 
+static bool weights_ok(const Ctx& c, const uint16_t* const home[3],
+                       const uint16_t* const pool[3], int p0, int p1) {
+  if (!home || !pool) return false;
+  for (int p = p0; p < p1; ++p) {
+    if (!home[p] || !aligned(home[p], 16)) return false;
+    if (c.d.B > 0 && (!pool[p] || !aligned(pool[p], 16))) return false;
+  }
+  return true;
+}
+
+moonep_status_t moonep_expert_gateup(moonep_handle_t h, const moonep_plan_t* plan,
+                                     int32_t rank, const uint16_t* x_nvs,
+                                     const uint16_t* const home[3],
+                                     const uint16_t* const pool[3], uint16_t* z_nvs,
+                                     hipStream_t stream) {
+  if (!h || !plan_ok(plan) || !x_nvs || !z_nvs) return MOONEP_ERR_ARG;
+  if (rank < -1 || rank >= h->c.d.R) return MOONEP_ERR_ARG;
+  if (!aligned(x_nvs, 16) || !aligned(z_nvs, 16) || (void*)z_nvs == (void*)x_nvs)
+    return MOONEP_ERR_ARG;
+  if (!weights_ok(h->c, home, pool, 0, 2)) return MOONEP_ERR_ARG;
+  return hip_status(launch_gateup(h->c, *plan, rank, x_nvs, home, pool, z_nvs, stream));
+}
+
+moonep_status_t moonep_expert_down(moonep_handle_t h, const moonep_plan_t* plan,
+                                   int32_t rank, const uint16_t* z_nvs,
+                                   const uint16_t* const home[3],
+                                   const uint16_t* const pool[3], uint16_t* y_nvs,
+                                   hipStream_t stream) {
+  if (!h || !plan_ok(plan) || !z_nvs || !y_nvs) return MOONEP_ERR_ARG;
+  if (rank < -1 || rank >= h->c.d.R) return MOONEP_ERR_ARG;
+  if (!aligned(z_nvs, 16) || !aligned(y_nvs, 16) || (void*)z_nvs == (void*)y_nvs)
+    return MOONEP_ERR_ARG;
+  if (!weights_ok(h->c, home, pool, 2, 3)) return MOONEP_ERR_ARG;
+  return hip_status(launch_down(h->c, *plan, rank, z_nvs, home, pool, y_nvs, stream));
+}
+
 moonep_status_t moonep_expert_ffn(moonep_handle_t h, const moonep_plan_t* plan,
                                   int32_t rank, const uint16_t* x_nvs,
                                   const uint16_t* const home[3],
                                   const uint16_t* const pool[3], uint16_t* z_ws,
                                   uint16_t* y_nvs, hipStream_t stream) {
-  if (!h || !plan_ok(plan) || !x_nvs || !z_ws || !y_nvs || !home || !pool)
-    return MOONEP_ERR_ARG;
+  if (!h || !plan_ok(plan) || !x_nvs || !z_ws || !y_nvs) return MOONEP_ERR_ARG;
   if (rank < -1 || rank >= h->c.d.R) return MOONEP_ERR_ARG;
   if (!aligned(x_nvs, 16) || !aligned(z_ws, 16) || !aligned(y_nvs, 16)) return MOONEP_ERR_ARG;
   if ((void*)z_ws == (void*)x_nvs || (void*)z_ws == (void*)y_nvs) return MOONEP_ERR_ARG;
-  for (int p = 0; p < 3; ++p) {
-    if (!home[p] || !aligned(home[p], 16)) return MOONEP_ERR_ARG;
-    if (h->c.d.B > 0 && (!pool[p] || !aligned(pool[p], 16))) return MOONEP_ERR_ARG;
-  }
-  return hip_status(launch_ffn(h->c, *plan, rank, x_nvs, home, pool, z_ws, y_nvs, stream));
+  if (!weights_ok(h->c, home, pool, 0, 3)) return MOONEP_ERR_ARG;
+  hipError_t e = launch_gateup(h->c, *plan, rank, x_nvs, home, pool, z_ws, stream);
+  if (e == hipSuccess) e = launch_down(h->c, *plan, rank, z_ws, home, pool, y_nvs, stream);
+  return hip_status(e);
 }
 
 moonep_status_t moonep_expert_wgrad(moonep_handle_t h, const moonep_plan_t* plan,

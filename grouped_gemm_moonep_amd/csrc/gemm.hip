@@ -21,14 +21,17 @@
 //
 // CDNA4 mapping: 256 threads = 4 waves in a 2x2 grid, each wave a 128x128
 // sub-tile as 4x4 v_mfma_f32_32x32x16_bf16 blocks (256 fp32 accumulators per
-// lane).  K advances 64 per step through two 72 KiB LDS stages (A rows and
-// B^T rows of 64 k, padded to 144 B so that MFMA fragment reads are
-// bank-conflict free).  Global loads are buffer loads
-// (out-of-range offsets read zero: no branches at tile edges), issued one
-// step ahead into registers; fragments are double-buffered in registers so
-// LDS latency hides behind MFMAs; one barrier per step.  Operands whose
-// contraction index is not contiguous in memory (gate/up weights, both wgrad
-// operands) are transposed 8x8 in registers (v_perm) on their way into LDS.
+// lane, in AGPRs).  K advances 32 per step through a ring of four 32 KiB LDS
+// stages filled by LDS-DMA buffer loads issued three steps ahead (no staging
+// registers, no LDS write instructions).  Operands contiguous along K are
+// kept as 64-byte rows with an XOR chunk swizzle and read with ds_read_b128;
+// operands stored [k][n] (gate/up weights, both weight-gradient operands) are
+// kept as 256-byte k-rows and read with the gfx950 transposing LDS read
+// (ds_read_b64_tr_b16), which hands each lane one column's 4 consecutive k.
+// Fragments are double-buffered in registers and every load and fragment
+// read is slotted between MFMAs, so the matrix unit stays busy across the one
+// barrier per step.  Buffer descriptors make tile edges branch-free
+// (out-of-range loads read zero, out-of-range stores are dropped).
 // Workgroup ids are remapped so that every XCD (own L2) works through a
 // contiguous range of tiles: neighbouring tiles share weight or activation
 // slabs in that XCD's L2.
@@ -144,12 +147,14 @@ struct RowTile {
       voff[i] = r < rows_valid ? (uint32_t)(r * ld * 2 + c * 16) : kOob;
     }
   }
+  __device__ __forceinline__ uint32_t koff(int64_t k0) const { return (uint32_t)(k0 * 2); }
+  // load i (0..3) of this wave for the k-block at byte offset ko
+  __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t ko, bool valid) {
+    load_lds(rs, tile + (wave_id() * 4 + i) * 1024, valid ? voff[i] + ko : kOob);
+  }
   __device__ __forceinline__ void issue(lds_t* tile, int64_t k0, bool valid) {
-    const int w = wave_id();
-    const uint32_t ko = (uint32_t)(k0 * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      load_lds(rs, tile + (w * 4 + i) * 1024, valid ? voff[i] + ko : kOob);
+    for (int i = 0; i < 4; ++i) issue1(tile, i, koff(k0), valid);
   }
   // 8 consecutive k (sub-step kk, lane half lh) of tile row `row`
   __device__ __forceinline__ static bf16x8 frag(const lds_t* tile, int row, int kk, int lh) {
@@ -180,14 +185,14 @@ struct ColTile {
       voff[i] = col < nv ? (uint32_t)(k * ld * 2 + col * 2) : kOob;
     }
   }
+  __device__ __forceinline__ uint32_t koff(int64_t k0) const { return (uint32_t)(k0 * ld2); }
+  __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t ko, bool valid) {
+    const int b = wave_id() * 4 + i;
+    load_lds((b >> 3) ? rs1 : rs0, tile + b * 1024, valid ? voff[i] + ko : kOob);
+  }
   __device__ __forceinline__ void issue(lds_t* tile, int64_t k0, bool valid) {
-    const int w = wave_id();
-    const uint32_t ko = (uint32_t)(k0 * ld2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = w * 4 + i;
-      load_lds((b >> 3) ? rs1 : rs0, tile + b * 1024, valid ? voff[i] + ko : kOob);
-    }
+    for (int i = 0; i < 4; ++i) issue1(tile, i, koff(k0), valid);
   }
   // 8 consecutive k (sub-step kk, lane half lh) of tile column n (the lane's)
   __device__ __forceinline__ static bf16x8 frag(const lds_t* tile, int nb, int kk, int lh) {
@@ -213,28 +218,35 @@ struct Frags {
   bf16x8 a[4], b[4];
 };
 
+// Fragment q of a sub-step, in the order the MFMAs consume them: A0, B0..B3,
+// A1..A3 (the MFMAs run i-major, so A0 and all of B are needed first).
 template <class TA, class TB>
-__device__ __forceinline__ void read_frags(Frags& f, const lds_t* stage, int kk, int arow0,
-                                           const int nrow[4]) {
+__device__ __forceinline__ void read_frag(Frags& f, int q, const lds_t* stage, int kk, int arow0,
+                                          const int nrow[4]) {
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
   const lds_t* A = stage;
   const lds_t* Bt = stage + kTileBytes;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
+  if (q == 0 || q >= 5) {
+    const int i = q == 0 ? 0 : q - 4;
     f.a[i] = TA::kRows ? RowTile::frag(A, arow0 + i * 32 + lr, kk, lh)
                        : ColTile::frag(A, arow0 + i * 32, kk, lh);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
+  } else {
+    const int j = q - 1;
     f.b[j] = TB::kRows ? RowTile::frag(Bt, nrow[j] + lr, kk, lh)
                        : ColTile::frag(Bt, nrow[j], kk, lh);
+  }
 }
 
-__device__ __forceinline__ void mma16(f32x16 acc[4][4], const Frags& f) {
+template <class TA, class TB>
+__device__ __forceinline__ void read_frags(Frags& f, const lds_t* stage, int kk, int arow0,
+                                           const int nrow[4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  for (int q = 0; q < 8; ++q) read_frag<TA, TB>(f, q, stage, kk, arow0, nrow);
+}
+
+__device__ __forceinline__ void mma1(f32x16 acc[4][4], const Frags& f, int idx) {
+  const int i = idx >> 2, j = idx & 3;
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
 // Wait until at most N LDS-DMA loads of this wave are outstanding.
@@ -246,13 +258,15 @@ __device__ __forceinline__ void wait_loads() {
   else static_assert(N == 0, "unsupported count");
 }
 
-constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
-#define MOONEP_SG(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+// Workgroup barrier without the LDS wait that __syncthreads() implies:
+// fragment reads issued just before it stay in flight (their consumers wait
+// for them).  The memory clobber keeps every LDS access on its side.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+#define MOONEP_PIN() __builtin_amdgcn_sched_barrier(0)
 
 // The four LDS stages are four separate arrays and the K loop is unrolled by
-// four, so every LDS access names its stage statically: the compiler can
-// then see that a fragment read never aliases an LDS-DMA load still in
-// flight into another stage and inserts no wait for it.
+// four, so every LDS access names its stage statically.
 struct Stages {
   lds_t* p[kStages];
 };
@@ -264,39 +278,54 @@ struct Stages {
   __shared__ __attribute__((aligned(16))) char name##3_[kStageBytes];      \
   const Stages name = {{(lds_t*)name##0_, (lds_t*)name##1_, (lds_t*)name##2_, (lds_t*)name##3_}}
 
-// One 32-deep step kt, held in stage S = kt % 4: sub-step 0 reads sub-step
-// 1's fragments while 16 MFMAs run; wait for the next step's loads, one
-// barrier, issue the loads of step kt+3 into stage (S+3)%4 (retired by the
-// barrier); sub-step 1 reads the next step's first fragments while its 16
-// MFMAs run.  Loads past the last step read nothing (out-of-range offset), so
-// the wait counts stay fixed.
+// One 32-deep step kt, held in stage S = kt % 4, as two runs of 16 MFMAs with
+// every other instruction slotted between them (an MFMA occupies the matrix
+// unit for 8 issue cycles of its wave, which covers a load's address
+// arithmetic and issue):
+//   run 1: MFMAs on f0 (sub-step 0); between the first eight, the eight
+//          fragment reads of sub-step 1 (stage S) into f1;
+//   wait for this wave's loads of step kt+1, barrier (every wave's loads of
+//          step kt+1 have landed; every wave is done reading step kt-1);
+//   run 2: MFMAs on f1; between the first eight, the eight LDS-DMA loads of
+//          step kt+3 into stage (S+3)%4 and the fragment reads of step kt+1's
+//          sub-step 0 (stage S+1) into f0.
+// Loads past the last step use an out-of-range offset (they read nothing and
+// keep the wait counts fixed).
 template <int S, class TA, class TB>
 __device__ __forceinline__ void kstep(TA& la, TB& lb, const Stages& st, int kt, int nk,
                                       Frags& f0, Frags& f1, f32x16 acc[4][4], int arow0,
                                       const int nrow[4]) {
   constexpr int N = (S + 1) % kStages, L = (S + kStages - 1) % kStages;
-  __builtin_amdgcn_sched_barrier(0);
-  read_frags<TA, TB>(f1, st.p[S], 1, arow0, nrow);
-  mma16(acc, f0);
-  MOONEP_SG(kSgDsRead, 16);
-  MOONEP_SG(kSgMfma, 16);
-  __builtin_amdgcn_sched_barrier(0);
+  MOONEP_PIN();
+#pragma unroll
+  for (int idx = 0; idx < 16; ++idx) {
+    mma1(acc, f0, idx);
+    if (idx < 8) read_frag<TA, TB>(f1, idx, st.p[S], 1, arow0, nrow);
+    MOONEP_PIN();
+  }
   wait_loads<kLoadsPerStep>();
-  __syncthreads();
+  barrier_only();
+  MOONEP_PIN();
   const int nx = kt + kStages - 1;
-  la.issue(st.p[L], (int64_t)nx * BK, nx < nk);
-  lb.issue(st.p[L] + kTileBytes, (int64_t)nx * BK, nx < nk);
-  __builtin_amdgcn_sched_barrier(0);
-  read_frags<TA, TB>(f0, st.p[N], 0, arow0, nrow);
-  mma16(acc, f1);
-  MOONEP_SG(kSgDsRead, 16);
-  MOONEP_SG(kSgMfma, 16);
-  __builtin_amdgcn_sched_barrier(0);
+  const bool valid = nx < nk;
+  const uint32_t koa = la.koff((int64_t)nx * BK), kob = lb.koff((int64_t)nx * BK);
+#pragma unroll
+  for (int idx = 0; idx < 16; ++idx) {
+    mma1(acc, f1, idx);
+    if (idx < 8) {
+      if (idx < 4) la.issue1(st.p[L], idx, koa, valid);
+      else lb.issue1(st.p[L] + kTileBytes, idx - 4, kob, valid);
+      read_frag<TA, TB>(f0, idx, st.p[N], 0, arow0, nrow);
+    }
+    MOONEP_PIN();
+  }
 }
 
 // The K loop shared by every GEMM here: a ring of 4 LDS stages filled by
 // LDS-DMA loads issued 3 steps ahead (no staging registers, no LDS write
-// instructions), one barrier per step.
+// instructions), one barrier per step.  The step count is rounded up to a
+// multiple of 4 so the loop has no remainder: the extra steps load nothing
+// (out-of-range offsets fill their stages with zeros) and add zero products.
 template <class TA, class TB>
 __device__ __forceinline__ void gemm_loop(TA& la, TB& lb, const Stages& st, int nk,
                                           f32x16 acc[4][4], int arow0, const int nrow[4]) {
@@ -307,20 +336,19 @@ __device__ __forceinline__ void gemm_loop(TA& la, TB& lb, const Stages& st, int 
     lb.issue(st.p[s] + kTileBytes, (int64_t)s * BK, s < nk);
   }
   wait_loads<2 * kLoadsPerStep>();
-  __syncthreads();
+  barrier_only();
   Frags f0, f1;
   read_frags<TA, TB>(f0, st.p[0], 0, arow0, nrow);
-  int kt = 0;
-  for (; kt + kStages <= nk; kt += kStages) {
+  const int nk4 = (nk + kStages - 1) / kStages * kStages;
+  for (int kt = 0; kt < nk4; kt += kStages) {
     kstep<0>(la, lb, st, kt + 0, nk, f0, f1, acc, arow0, nrow);
     kstep<1>(la, lb, st, kt + 1, nk, f0, f1, acc, arow0, nrow);
     kstep<2>(la, lb, st, kt + 2, nk, f0, f1, acc, arow0, nrow);
     kstep<3>(la, lb, st, kt + 3, nk, f0, f1, acc, arow0, nrow);
   }
-  if (kt < nk) kstep<0>(la, lb, st, kt, nk, f0, f1, acc, arow0, nrow);
-  if (kt + 1 < nk) kstep<1>(la, lb, st, kt + 1, nk, f0, f1, acc, arow0, nrow);
-  if (kt + 2 < nk) kstep<2>(la, lb, st, kt + 2, nk, f0, f1, acc, arow0, nrow);
   wait_loads<0>();
+  // every wave is past its last fragment read before the stages are reused
+  __syncthreads();
 }
 
 __device__ __forceinline__ void zero_acc(f32x16 acc[4][4]) {
@@ -348,10 +376,11 @@ struct Tile {
 };
 
 struct FfnArgs {
-  const uint16_t* x;        // [R*NvS][H]
+  const uint16_t* x;        // [R*NvS][H] (gate/up input)
   const uint16_t* home[3];  // [E][H][Hp]
   const uint16_t* pool[3];  // [R*B][H][Hp]
-  uint16_t* z;              // [R*NvS][Hp]
+  uint16_t* z;              // [R*NvS][Hp] (gate/up output)
+  const uint16_t* zin;      // [R*NvS][Hp] (down input)
   uint16_t* y;              // [R*NvS][H]
   const int32_t* tiles;     // [R][max_tiles][4]
   const int32_t* ntiles;    // [R]
@@ -495,7 +524,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   const int nrow[4] = {wn * 128, wn * 128 + 32, wn * 128 + 64, wn * 128 + 96};
 
   RowTile la, lb;
-  la.init(a.z + ((int64_t)d * a.NvS + tl.m0) * a.Hp, a.Hp, rows_valid);
+  la.init(a.zin + ((int64_t)d * a.NvS + tl.m0) * a.Hp, a.Hp, rows_valid);
   lb.init(weight_row(a, 2, d, tl.row) + (int64_t)n0 * a.Hp, a.Hp, cols_valid);
   f32x16 acc[4][4];
   zero_acc(acc);
@@ -591,26 +620,50 @@ int64_t pad_grid(int64_t n) { return (n + kXcds - 1) / kXcds * kXcds; }
 
 }  // namespace
 
-hipError_t launch_ffn(const Ctx& c, const moonep_plan_t& p, int rank, const uint16_t* x_nvs,
-                      const uint16_t* const home[3], const uint16_t* const pool[3], uint16_t* z,
-                      uint16_t* y, hipStream_t s) {
+static FfnArgs ffn_args(const Ctx& c, const moonep_plan_t& p, int rank,
+                        const uint16_t* const home[3], const uint16_t* const pool[3]) {
   const Dims& d = c.d;
-  gemm_schedule<<<d.R, 256, 0, s>>>(p.aux + d.aux.act, p.cu_seqlens, p.seg_tokens, c.tiles,
-                                   c.ntiles, 2 * d.L, d.E + d.B, d.tp, c.max_tiles);
   FfnArgs a;
-  a.x = x_nvs;
   for (int i = 0; i < 3; ++i) {
     a.home[i] = home[i];
     a.pool[i] = pool[i];
   }
-  a.z = z; a.y = y; a.tiles = c.tiles; a.ntiles = c.ntiles;
+  a.x = nullptr; a.z = nullptr; a.zin = nullptr; a.y = nullptr;
+  a.tiles = p.aux + d.aux.tiles; a.ntiles = p.aux + d.aux.ntiles;
   a.R = d.R; a.E = d.E; a.B = d.B; a.H = d.H; a.Hp = d.Hp; a.NvS = (int)d.NvS;
-  a.max_tiles = c.max_tiles;
+  a.max_tiles = d.max_tiles;
   a.rank0 = rank < 0 ? 0 : rank;
   a.nranks = rank < 0 ? d.R : 1;
-  a.ntn = (d.Hp + 127) / 128;
+  a.ntn = 0;
+  return a;
+}
+
+hipError_t launch_gemm_schedule(const Ctx& c, const moonep_plan_t& p, hipStream_t s) {
+  const Dims& d = c.d;
+  gemm_schedule<<<d.R, 256, 0, s>>>(p.aux + d.aux.act, p.cu_seqlens, p.seg_tokens,
+                                   p.aux + d.aux.tiles, p.aux + d.aux.ntiles, 2 * d.L,
+                                   d.E + d.B, d.tp, d.max_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup(const Ctx& c, const moonep_plan_t& p, int rank, const uint16_t* x_nvs,
+                         const uint16_t* const home[3], const uint16_t* const pool[3],
+                         uint16_t* z, hipStream_t s) {
+  FfnArgs a = ffn_args(c, p, rank, home, pool);
+  a.x = x_nvs;
+  a.z = z;
+  a.ntn = (c.d.Hp + 127) / 128;
   ffn_gateup<<<(unsigned)pad_grid((int64_t)a.nranks * a.max_tiles * a.ntn), kThreads, 0, s>>>(a);
-  a.ntn = (d.H + BN - 1) / BN;
+  return hipGetLastError();
+}
+
+hipError_t launch_down(const Ctx& c, const moonep_plan_t& p, int rank, const uint16_t* z,
+                       const uint16_t* const home[3], const uint16_t* const pool[3],
+                       uint16_t* y, hipStream_t s) {
+  FfnArgs a = ffn_args(c, p, rank, home, pool);
+  a.zin = z;
+  a.y = y;
+  a.ntn = (c.d.H + BN - 1) / BN;
   ffn_down<<<(unsigned)pad_grid((int64_t)a.nranks * a.max_tiles * a.ntn), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }

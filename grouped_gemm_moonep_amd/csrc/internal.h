@@ -25,6 +25,8 @@ struct AuxLayout {
   int64_t dup_first;// [R*B] first holder of each
   int64_t dup_cnt;  // [R*B] holder count of each
   int64_t hold;     // [R*B] holder slots d*B+j grouped by expert, ascending d
+  int64_t tiles;    // [R][max_tiles][4] grouped-GEMM M-tiles (row, first slot, end slot, 0)
+  int64_t ntiles;   // [R] M-tiles of each rank
   int64_t total;
 };
 
@@ -33,6 +35,7 @@ struct Dims {
   int L;          // E / R
   int64_t NvS;    // slots per rank
   int nch;        // planning chunks per rank
+  int max_tiles;  // grouped-GEMM M-tiles per rank, upper bound
   AuxLayout aux;
 };
 
@@ -48,10 +51,6 @@ struct Ctx {
   int32_t* npieces;   // [R]
   int32_t* line;      // [E] line start a_e
   int32_t* chunk_err; // [R][nch] routing error bits found per chunk
-  // grouped GEMM schedule scratch (device)
-  int32_t* tiles;     // [R][max_tiles][4] (row, first slot, end slot, 0)
-  int32_t* ntiles;    // [R]
-  int max_tiles;      // per rank, for the FFN / wgrad M-tile size
 };
 
 bool dims_from_config(const moonep_config_t* cfg, Dims* out);
@@ -71,10 +70,13 @@ hipError_t launch_prefetch(const Ctx& c, const moonep_plan_t& p,
 hipError_t launch_reduce_grad(const Ctx& c, const moonep_plan_t& p,
                               float* const gh[3], float* const rb[3],
                               hipStream_t s);
-hipError_t launch_ffn(const Ctx& c, const moonep_plan_t& p, int rank,
-                      const uint16_t* x_nvs, const uint16_t* const home[3],
-                      const uint16_t* const pool[3], uint16_t* z,
-                      uint16_t* y, hipStream_t s);
+hipError_t launch_gemm_schedule(const Ctx& c, const moonep_plan_t& p, hipStream_t s);
+hipError_t launch_gateup(const Ctx& c, const moonep_plan_t& p, int rank,
+                         const uint16_t* x_nvs, const uint16_t* const home[3],
+                         const uint16_t* const pool[3], uint16_t* z, hipStream_t s);
+hipError_t launch_down(const Ctx& c, const moonep_plan_t& p, int rank,
+                       const uint16_t* z, const uint16_t* const home[3],
+                       const uint16_t* const pool[3], uint16_t* y, hipStream_t s);
 hipError_t launch_wgrad(const Ctx& c, const moonep_plan_t& p, int rank,
                         const uint16_t* a, const uint16_t* b, float* gh,
                         float* rb, hipStream_t s);

@@ -181,13 +181,34 @@ moonep_status_t moonep_prefetch_weight(moonep_handle_t h,
  *   Y = bf16_rne(Z Wd_i^T)    -> y_nvs [R,NvS,H],
  * with every projection stored [H,Hp] and rows resolved as in
  * moonep_prefetch_weight.  y_nvs may equal x_nvs (in-place, the README's
- * zero_copy); no other aliasing.  Slots outside segments are not written. */
+ * zero_copy); no other aliasing.  Slots outside segments are not written.
+ * The same as moonep_expert_gateup followed by moonep_expert_down. */
 moonep_status_t moonep_expert_ffn(moonep_handle_t h, const moonep_plan_t* plan,
                                   int32_t rank, const uint16_t* x_nvs,
                                   const uint16_t* const home[3],
                                   const uint16_t* const pool[3],
                                   uint16_t* z_ws, uint16_t* y_nvs,
                                   hipStream_t stream);
+
+/* First half of the grouped SwiGLU FFN (README "Usage > Integration"): the
+ * gate and up projections and the SwiGLU product,
+ * z_nvs = bf16_rne(silu(X Wg_i) * (X Wu_i)) per segment, as in
+ * moonep_expert_ffn.  Reads home[0..1] and pool[0..1] only (home[2],
+ * pool[2] may be NULL); z_nvs [R,NvS,Hp] must not alias x_nvs. */
+moonep_status_t moonep_expert_gateup(moonep_handle_t h, const moonep_plan_t* plan,
+                                     int32_t rank, const uint16_t* x_nvs,
+                                     const uint16_t* const home[3],
+                                     const uint16_t* const pool[3],
+                                     uint16_t* z_nvs, hipStream_t stream);
+
+/* Second half (README "Usage > Integration"): y_nvs = bf16_rne(Z Wd_i^T) per
+ * segment, Z = z_nvs [R,NvS,Hp], y_nvs [R,NvS,H] (must not alias z_nvs).
+ * Reads home[2] and pool[2] only (the other entries may be NULL). */
+moonep_status_t moonep_expert_down(moonep_handle_t h, const moonep_plan_t* plan,
+                                   int32_t rank, const uint16_t* z_nvs,
+                                   const uint16_t* const home[3],
+                                   const uint16_t* const pool[3],
+                                   uint16_t* y_nvs, hipStream_t stream);
 
 /* Weight gradient of one projection (README "Gradient buffer"): for rank d
  * (-1: all) and every row i with length > 0, dW_i += A_seg^T B_seg in fp32,

@@ -87,6 +87,10 @@ def test_null_arguments_rejected_on_host():
     assert lib.moonep_prefetch_weight(None, ctypes.byref(plan), P3(), P3(), None) == ERR
     assert lib.moonep_expert_ffn(None, ctypes.byref(plan), -1, None, P3(), P3(), None, None,
                                  None) == ERR
+    assert lib.moonep_expert_gateup(None, ctypes.byref(plan), -1, None, P3(), P3(), None,
+                                    None) == ERR
+    assert lib.moonep_expert_down(None, ctypes.byref(plan), -1, None, P3(), P3(), None,
+                                  None) == ERR
     assert lib.moonep_expert_wgrad(None, ctypes.byref(plan), -1, None, None, None, None,
                                    None) == ERR
     assert lib.moonep_reduce_grad(None, ctypes.byref(plan), P3(), P3(), None) == ERR

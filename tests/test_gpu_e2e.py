@@ -176,3 +176,29 @@ def test_ffn_full_size_sampled(name, target):
         assert_close_bf16(host_bf16(z[d, slots]), zw, what=f"z d={d} row={row}")
         assert_close_bf16(host_bf16(y[d, slots]), yw, what=f"y d={d} row={row}")
     buf.destroy()
+
+
+def test_gateup_then_down_equals_ffn():
+    """moonep_expert_gateup + moonep_expert_down are the two launches of
+    moonep_expert_ffn: identical bits, and each touches only its output."""
+    w = synth.WORKLOADS["mid_r8_s1024_k4_e32"]
+    topk, rw, x, home_h = _setup(w, 2.0)
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    home = [dev_bf16(h) for h in home_h]
+    pool = _pool_dev(w)
+    buf.prefetch_weight(plan, home, pool)
+    x_nvs, _ = buf.dispatch(plan, dev_bf16(x))
+    z1, y1 = buf.expert_ffn(plan, x_nvs, home, pool)
+    z2 = torch.full_like(z1, 0).view(torch.int16).fill_(SENT).view(torch.bfloat16)
+    buf.expert_gateup(plan, x_nvs, [home[0], home[1], None], [pool[0], pool[1], None], z2)
+    y2 = torch.full_like(y1, 0).view(torch.int16).fill_(SENT).view(torch.bfloat16)
+    buf.expert_down(plan, z2, [None, None, home[2]], [None, None, pool[2]], y2)
+    p = oracle.plan(topk, w.E, w.B, w.token_padding)
+    z1h, z2h, y1h, y2h = host_bf16(z1), host_bf16(z2), host_bf16(y1), host_bf16(y2)
+    for d in range(w.R):
+        end = p.cu_seqlens[d, -1]
+        assert np.array_equal(z1h[d, :end], z2h[d, :end])
+        assert np.array_equal(y1h[d, :end], y2h[d, :end])
+        assert (z2h[d, end:] == SENT).all() and (y2h[d, end:] == SENT).all()
+    buf.destroy()
