@@ -21,20 +21,21 @@
 //
 // CDNA4 mapping: 256 threads = 4 waves in a 2x2 grid, each wave a 128x128
 // sub-tile as 4x4 v_mfma_f32_32x32x16_bf16 blocks (256 fp32 accumulators per
-// lane, in AGPRs).  K advances 32 per step through a ring of four 32 KiB LDS
-// stages filled by LDS-DMA buffer loads issued three steps ahead (no staging
-// registers, no LDS write instructions).  Operands contiguous along K are
-// kept as 64-byte rows with an XOR chunk swizzle and read with ds_read_b128;
-// operands stored [k][n] (gate/up weights, both weight-gradient operands) are
-// kept as 256-byte k-rows and read with the gfx950 transposing LDS read
-// (ds_read_b64_tr_b16), which hands each lane one column's 4 consecutive k.
-// Fragments are double-buffered in registers and every load and fragment
-// read is slotted between MFMAs, so the matrix unit stays busy across the one
-// barrier per step.  Buffer descriptors make tile edges branch-free
-// (out-of-range loads read zero, out-of-range stores are dropped).
-// Workgroup ids are remapped so that every XCD (own L2) works through a
-// contiguous range of tiles: neighbouring tiles share weight or activation
-// slabs in that XCD's L2.
+// lane, in AGPRs).  K advances 64 per step.  Operand tiles (256 x 64 bf16,
+// 32 KiB) rotate through a ring of five LDS slots (160 KiB) filled by LDS-DMA
+// buffer loads (no staging registers, no LDS write instructions); weights are
+// fetched two steps ahead, activations one.  Operands contiguous along K are
+// kept as 128-byte rows (whole cache lines per load) with an XOR chunk
+// swizzle and read with ds_read_b128; operands stored [k][n] (gate/up
+// weights, both weight-gradient operands) are kept as 256-byte k-rows and read
+// with the gfx950 transposing LDS read (ds_read_b64_tr_b16), which hands each
+// lane one column's 4 consecutive k.  Fragments are double-buffered in
+// registers and every load and fragment read is slotted between MFMAs, so the
+// matrix unit stays busy across the one barrier per step.  Buffer descriptors
+// make tile edges branch-free (out-of-range loads read zero, out-of-range
+// stores are dropped).  Workgroup ids are remapped so that every XCD (own L2)
+// works through a contiguous range of tiles: neighbouring tiles share weight
+// or activation slabs in that XCD's L2.
 #include "internal.h"
 
 namespace moonep {
@@ -47,12 +48,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
-constexpr int BM = 256, BN = 256, BK = 32;        // K advances 32 per step
-constexpr int kStages = 4;                        // LDS ring depth
-constexpr int kTileBytes = 256 * BK * 2;          // 16 KiB per operand tile
-constexpr int kStageBytes = 2 * kTileBytes;       // A tile + B tile
+constexpr int BM = 256, BN = 256, BK = 64;        // K advances 64 per step
 constexpr int kXcds = 8;
-constexpr int kLoadsPerStep = 8;                  // LDS-DMA loads per wave per step
+constexpr int kLoadsPerStep = 8;                  // LDS-DMA loads per wave per tile and step
+constexpr int kTileOffB = 0;                      // B tile offset inside its slot
 
 typedef __attribute__((address_space(3))) char lds_t;
 
@@ -118,86 +117,87 @@ __device__ __forceinline__ void bstore16(Rsrc r, uint32_t voff, unsigned v) {
 }
 
 // ---------------------------------------------------------------------------
-// Operand tiles in LDS (one per stage and operand, 16 KiB each).
+// Operand tiles in LDS: 256 rows (or columns) x 64 k of bf16 = 32 KiB, one
+// per ring slot.
 //
-// Row tile (operand contiguous along k): 256 rows x 32 k, rows of 64 B; the
-// 16-byte chunk c of row r sits at chunk c ^ ((r >> 2) & 3), so the 16 rows
-// read by a 16-lane group of an MFMA fragment load hit 16 distinct bank
-// groups.  One LDS-DMA load (a wave, 1 KiB) fills 16 rows.
+// Row tile (operand contiguous along k): rows of 128 B (64 k); the 16-byte
+// chunk c of row r sits at position c ^ (r & 7), so the 8 rows read together
+// by an MFMA fragment load hit 8 distinct bank groups.  One LDS-DMA load (a
+// wave, 1 KiB) fills 8 rows, each a whole 128-byte cache line: the L1/L2 path
+// costs per cache line touched, and half-line rows would halve its rate.
 //
 // Column tile (operand stored [k][n], n contiguous): two regions of 128
-// columns (gate and up weights, or two column halves of one matrix), 32 k
-// rows of 256 B each; chunk c of row k sits at chunk c ^ (4 (k & 3)).  One
+// columns (gate and up weights, or two column halves of one matrix), 64 k
+// rows of 256 B each; chunk c of row k sits at position c ^ (4 (k & 3)).  One
 // LDS-DMA load fills 4 rows of one region.  Fragments are read with the
 // gfx950 transposing LDS read (ds_read_b64_tr_b16): lane q of a 16-lane
 // group points at row k0 + q/4, columns n0 + 4 (q%4) .. +3, and lane i then
 // holds column n0 + i, rows k0 .. k0+3 -- the MFMA operand layout.
+constexpr int kSlotBytes = 256 * BK * 2;          // 32 KiB
+constexpr int kSlots = 5;                         // 160 KiB ring
+
 struct RowTile {
   static constexpr bool kRows = true;
   DmaRsrc rs;
-  uint32_t voff[4];
-  // base: row 0, k 0 of the tile; ld: row stride (elements)
+  uint32_t voff;        // this lane's offset for load 0 of k-block 0
+  uint32_t step;        // byte distance between consecutive loads of a wave (8 rows)
+  // base: row 0, k 0 of the tile; ld: row stride (elements).  Rows at or
+  // past rows_valid lie outside the descriptor's range and read zero.
   __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int rows_valid) {
     const int w = wave_id(), lane = threadIdx.x & 63;
     rs = make_dma_rsrc(base, (int64_t)rows_valid * ld * 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * (w * 4 + i) + (lane >> 2);
-      const int c = (lane & 3) ^ ((r >> 2) & 3);
-      voff[i] = r < rows_valid ? (uint32_t)(r * ld * 2 + c * 16) : kOob;
-    }
+    const int r = 64 * w + (lane >> 3);
+    const int c = (lane & 7) ^ (r & 7);
+    voff = (uint32_t)(r * ld * 2 + c * 16);
+    step = (uint32_t)(16 * ld);
   }
   __device__ __forceinline__ uint32_t koff(int64_t k0) const { return (uint32_t)(k0 * 2); }
-  // load i (0..3) of this wave for the k-block at byte offset ko
-  __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t ko, bool valid) {
-    load_lds(rs, tile + (wave_id() * 4 + i) * 1024, valid ? voff[i] + ko : kOob);
+  // load i (0..7) of this wave for the k-block at byte offset ko
+  __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t ko, bool valid) const {
+    const uint32_t s = __builtin_amdgcn_readfirstlane(valid ? ko + (uint32_t)i * step : kOob);
+    load_lds(rs, tile + (wave_id() * 8 + i) * 1024, voff + s);
   }
-  __device__ __forceinline__ void issue(lds_t* tile, int64_t k0, bool valid) {
+  __device__ __forceinline__ void issue(lds_t* tile, int64_t k0, bool valid) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) issue1(tile, i, koff(k0), valid);
+    for (int i = 0; i < 8; ++i) issue1(tile, i, koff(k0), valid);
   }
-  // 8 consecutive k (sub-step kk, lane half lh) of tile row `row`
+  // 8 consecutive k (sub-step kk of 4, lane half lh) of tile row `row`
   __device__ __forceinline__ static bf16x8 frag(const lds_t* tile, int row, int kk, int lh) {
-    const int c = (2 * kk + lh) ^ ((row >> 2) & 3);
-    return *(const __attribute__((address_space(3))) bf16x8*)(tile + row * 64 + c * 16);
+    const int c = (2 * kk + lh) ^ (row & 7);
+    return *(const __attribute__((address_space(3))) bf16x8*)(tile + row * 128 + c * 16);
   }
 };
 
 struct ColTile {
   static constexpr bool kRows = false;
-  DmaRsrc rs0, rs1;
-  uint32_t voff[4];
+  DmaRsrc rs;           // this wave's region (waves 0,1: region 0; waves 2,3: region 1)
+  uint32_t voff;        // this lane's offset for load 0 of k-block 0 (out of range past nv)
   uint32_t ld2;
   // src0/src1: k 0, n 0 of the two 128-column regions; ld: k stride
   // (elements); k_total: valid k rows from k 0; nv0/nv1: valid columns
   __device__ __forceinline__ void init(const uint16_t* src0, const uint16_t* src1, int64_t ld,
                                        int64_t k_total, int nv0, int nv1) {
     const int w = wave_id(), lane = threadIdx.x & 63;
-    rs0 = make_dma_rsrc(src0, k_total * ld * 2);
-    rs1 = make_dma_rsrc(src1, k_total * ld * 2);
+    const int region = w >> 1;
+    rs = make_dma_rsrc(region ? src1 : src0, k_total * ld * 2);
     ld2 = (uint32_t)(ld * 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = w * 4 + i;                       // region b >> 3
-      const int k = 4 * (b & 7) + (lane >> 4);
-      const int col = 8 * ((lane & 15) ^ (4 * (k & 3)));
-      const int nv = (b >> 3) ? nv1 : nv0;
-      voff[i] = col < nv ? (uint32_t)(k * ld * 2 + col * 2) : kOob;
-    }
+    const int k = 32 * (w & 1) + (lane >> 4);        // load i adds 4 i rows
+    const int col = 8 * ((lane & 15) ^ (4 * (k & 3)));
+    voff = col < (region ? nv1 : nv0) ? (uint32_t)(k * ld * 2 + col * 2) : kOob;
   }
   __device__ __forceinline__ uint32_t koff(int64_t k0) const { return (uint32_t)(k0 * ld2); }
-  __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t ko, bool valid) {
-    const int b = wave_id() * 4 + i;
-    load_lds((b >> 3) ? rs1 : rs0, tile + b * 1024, valid ? voff[i] + ko : kOob);
+  __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t ko, bool valid) const {
+    const uint32_t s = __builtin_amdgcn_readfirstlane(valid ? ko + (uint32_t)(4 * i) * ld2 : kOob);
+    load_lds(rs, tile + (wave_id() * 8 + i) * 1024, voff + s);
   }
-  __device__ __forceinline__ void issue(lds_t* tile, int64_t k0, bool valid) {
+  __device__ __forceinline__ void issue(lds_t* tile, int64_t k0, bool valid) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) issue1(tile, i, koff(k0), valid);
+    for (int i = 0; i < 8; ++i) issue1(tile, i, koff(k0), valid);
   }
-  // 8 consecutive k (sub-step kk, lane half lh) of tile column n (the lane's)
+  // 8 consecutive k (sub-step kk of 4, lane half lh) of tile column n (the lane's)
   __device__ __forceinline__ static bf16x8 frag(const lds_t* tile, int nb, int kk, int lh) {
     const int lane = threadIdx.x & 63, q = lane & 15, g = (lane >> 4) & 1;
-    const lds_t* region = tile + (nb >> 7) * 8192;
+    const lds_t* region = tile + (nb >> 7) * 16384;
     const int col = (nb & 127) + 16 * g + 4 * (q & 3);
     i16x4 h[2];
 #pragma unroll
@@ -221,11 +221,9 @@ struct Frags {
 // Fragment q of a sub-step, in the order the MFMAs consume them: A0, B0..B3,
 // A1..A3 (the MFMAs run i-major, so A0 and all of B are needed first).
 template <class TA, class TB>
-__device__ __forceinline__ void read_frag(Frags& f, int q, const lds_t* stage, int kk, int arow0,
-                                          const int nrow[4]) {
+__device__ __forceinline__ void read_frag(Frags& f, int q, const lds_t* A, const lds_t* Bt,
+                                          int kk, int arow0, const int nrow[4]) {
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
-  const lds_t* A = stage;
-  const lds_t* Bt = stage + kTileBytes;
   if (q == 0 || q >= 5) {
     const int i = q == 0 ? 0 : q - 4;
     f.a[i] = TA::kRows ? RowTile::frag(A, arow0 + i * 32 + lr, kk, lh)
@@ -235,13 +233,6 @@ __device__ __forceinline__ void read_frag(Frags& f, int q, const lds_t* stage, i
     f.b[j] = TB::kRows ? RowTile::frag(Bt, nrow[j] + lr, kk, lh)
                        : ColTile::frag(Bt, nrow[j], kk, lh);
   }
-}
-
-template <class TA, class TB>
-__device__ __forceinline__ void read_frags(Frags& f, const lds_t* stage, int kk, int arow0,
-                                           const int nrow[4]) {
-#pragma unroll
-  for (int q = 0; q < 8; ++q) read_frag<TA, TB>(f, q, stage, kk, arow0, nrow);
 }
 
 __device__ __forceinline__ void mma1(f32x16 acc[4][4], const Frags& f, int idx) {
@@ -254,100 +245,102 @@ template <int N>
 __device__ __forceinline__ void wait_loads() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   else static_assert(N == 0, "unsupported count");
 }
 
-// Workgroup barrier without the LDS wait that __syncthreads() implies:
-// fragment reads issued just before it stay in flight (their consumers wait
-// for them).  The memory clobber keeps every LDS access on its side.
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+// Workgroup barrier after this wave's LDS reads have completed (it writes no
+// LDS itself: other waves may then overwrite what it read).  Fragment
+// registers already loaded are not waited for again.
+__device__ __forceinline__ void barrier_reads_done() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 #define MOONEP_PIN() __builtin_amdgcn_sched_barrier(0)
 
-// The four LDS stages are four separate arrays and the K loop is unrolled by
-// four, so every LDS access names its stage statically.
-struct Stages {
-  lds_t* p[kStages];
+// The ring: kSlots slots of 32 KiB; step j's A tile sits in slot (2j+1) % 5,
+// its B tile in slot 2j % 5.  Hence A(j) reuses the slot of B(j-2) and B(j)
+// the slot of A(j-3): B tiles (weights) are loaded two steps ahead, A tiles
+// one step ahead.  The K loop is unrolled over the ring period, so every slot
+// address is a constant.
+struct Ring {
+  lds_t* base;
+  template <int J>
+  __device__ __forceinline__ lds_t* a() const { return base + ((2 * J + 1) % kSlots) * kSlotBytes; }
+  template <int J>
+  __device__ __forceinline__ lds_t* b() const { return base + ((2 * J) % kSlots) * kSlotBytes; }
 };
 
-#define MOONEP_STAGE_ARRAYS(name)                                           \
-  __shared__ __attribute__((aligned(16))) char name##0_[kStageBytes];      \
-  __shared__ __attribute__((aligned(16))) char name##1_[kStageBytes];      \
-  __shared__ __attribute__((aligned(16))) char name##2_[kStageBytes];      \
-  __shared__ __attribute__((aligned(16))) char name##3_[kStageBytes];      \
-  const Stages name = {{(lds_t*)name##0_, (lds_t*)name##1_, (lds_t*)name##2_, (lds_t*)name##3_}}
+#define MOONEP_RING(name)                                                          \
+  __shared__ __attribute__((aligned(16))) char name##_[kSlots * kSlotBytes];       \
+  const Ring name = {(lds_t*)name##_}
 
-// One 32-deep step kt, held in stage S = kt % 4, as two runs of 16 MFMAs with
-// every other instruction slotted between them (an MFMA occupies the matrix
-// unit for 8 issue cycles of its wave, which covers a load's address
-// arithmetic and issue):
-//   run 1: MFMAs on f0 (sub-step 0); between the first eight, the eight
-//          fragment reads of sub-step 1 (stage S) into f1;
-//   wait for this wave's loads of step kt+1, barrier (every wave's loads of
-//          step kt+1 have landed; every wave is done reading step kt-1);
-//   run 2: MFMAs on f1; between the first eight, the eight LDS-DMA loads of
-//          step kt+3 into stage (S+3)%4 and the fragment reads of step kt+1's
-//          sub-step 0 (stage S+1) into f0.
-// Loads past the last step use an out-of-range offset (they read nothing and
-// keep the wait counts fixed).
-template <int S, class TA, class TB>
-__device__ __forceinline__ void kstep(TA& la, TB& lb, const Stages& st, int kt, int nk,
+// One 64-deep step j (J = j mod 5) = 64 MFMAs per wave in four 16-deep
+// sub-steps, with every other instruction slotted between MFMAs (an MFMA
+// occupies the matrix unit for 8 issue cycles of its wave):
+//   sub-steps 0..2 read the next sub-step's fragments while computing;
+//   the 8 loads of A(j+1) go out after MFMAs 1, 4, ..., 22 and the 8 loads
+//   of B(j+2) after MFMAs 26, 30, ..., 54, one load per three or four MFMAs;
+//   after MFMA 55: wait for A(j+1) and B(j+1) (the 8 most recent loads are
+//   B(j+2)'s), wait for this wave's LDS reads, barrier;
+//   MFMAs 56..63 read step j+1's first fragments.
+// The barrier orders, for every wave, all reads of step j before any load
+// issued after it, and the arrival of step j+1's tiles before any read of
+// them.  A(j+2) then reuses B(j)'s slot and B(j+3) reuses A(j)'s.
+template <int J, class TA, class TB>
+__device__ __forceinline__ void kstep(const TA& la, const TB& lb, const Ring& ring, int j, int nk,
                                       Frags& f0, Frags& f1, f32x16 acc[4][4], int arow0,
                                       const int nrow[4]) {
-  constexpr int N = (S + 1) % kStages, L = (S + kStages - 1) % kStages;
+  constexpr int J1 = (J + 1) % kSlots, J2 = (J + 2) % kSlots;
+  const lds_t* A = ring.a<J>();
+  const lds_t* Bt = ring.b<J>();
+  const lds_t* An = ring.a<J1>();
+  const lds_t* Bn = ring.b<J1>();
+  lds_t* la_dst = ring.a<J1>();
+  lds_t* lb_dst = ring.b<J2>();
+  const uint32_t koa = la.koff((int64_t)(j + 1) * BK), kob = lb.koff((int64_t)(j + 2) * BK);
+  const bool va = j + 1 < nk, vb = j + 2 < nk;
   MOONEP_PIN();
 #pragma unroll
-  for (int idx = 0; idx < 16; ++idx) {
-    mma1(acc, f0, idx);
-    if (idx < 8) read_frag<TA, TB>(f1, idx, st.p[S], 1, arow0, nrow);
-    MOONEP_PIN();
-  }
-  wait_loads<kLoadsPerStep>();
-  barrier_only();
-  MOONEP_PIN();
-  const int nx = kt + kStages - 1;
-  const bool valid = nx < nk;
-  const uint32_t koa = la.koff((int64_t)nx * BK), kob = lb.koff((int64_t)nx * BK);
-#pragma unroll
-  for (int idx = 0; idx < 16; ++idx) {
-    mma1(acc, f1, idx);
-    if (idx < 8) {
-      if (idx < 4) la.issue1(st.p[L], idx, koa, valid);
-      else lb.issue1(st.p[L] + kTileBytes, idx - 4, kob, valid);
-      read_frag<TA, TB>(f0, idx, st.p[N], 0, arow0, nrow);
+  for (int p = 0; p < 64; ++p) {
+    const int sub = p >> 4, idx = p & 15;
+    mma1(acc, (sub & 1) ? f1 : f0, idx);
+    if (sub < 3 && idx < 8) read_frag<TA, TB>((sub & 1) ? f0 : f1, idx, A, Bt, sub + 1, arow0, nrow);
+    if (p % 3 == 1 && p <= 22) la.issue1(la_dst, p / 3, koa, va);
+    if (p >= 26 && p <= 54 && (p - 26) % 4 == 0) lb.issue1(lb_dst, (p - 26) / 4, kob, vb);
+    if (p == 55) {
+      MOONEP_PIN();
+      wait_loads<kLoadsPerStep>();
+      barrier_reads_done();
     }
+    if (p >= 56) read_frag<TA, TB>(f0, p - 56, An, Bn, 0, arow0, nrow);
     MOONEP_PIN();
   }
 }
 
-// The K loop shared by every GEMM here: a ring of 4 LDS stages filled by
-// LDS-DMA loads issued 3 steps ahead (no staging registers, no LDS write
-// instructions), one barrier per step.  The step count is rounded up to a
-// multiple of 4 so the loop has no remainder: the extra steps load nothing
-// (out-of-range offsets fill their stages with zeros) and add zero products.
+// The K loop shared by every GEMM here.  The prologue loads B(0), A(0),
+// B(1); each step then loads A(j+1) and B(j+2) (out-of-range offsets past
+// the last step: they read nothing and keep the wait counts fixed).
 template <class TA, class TB>
-__device__ __forceinline__ void gemm_loop(TA& la, TB& lb, const Stages& st, int nk,
+__device__ __forceinline__ void gemm_loop(const TA& la, const TB& lb, const Ring& ring, int nk,
                                           f32x16 acc[4][4], int arow0, const int nrow[4]) {
   if (nk <= 0) return;
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) {
-    la.issue(st.p[s], (int64_t)s * BK, s < nk);
-    lb.issue(st.p[s] + kTileBytes, (int64_t)s * BK, s < nk);
-  }
-  wait_loads<2 * kLoadsPerStep>();
-  barrier_only();
+  lb.issue(ring.b<0>(), 0, true);
+  la.issue(ring.a<0>(), 0, true);
+  lb.issue(ring.b<1>(), BK, 1 < nk);
+  wait_loads<kLoadsPerStep>();
+  barrier_reads_done();
   Frags f0, f1;
-  read_frags<TA, TB>(f0, st.p[0], 0, arow0, nrow);
-  const int nk4 = (nk + kStages - 1) / kStages * kStages;
-  for (int kt = 0; kt < nk4; kt += kStages) {
-    kstep<0>(la, lb, st, kt + 0, nk, f0, f1, acc, arow0, nrow);
-    kstep<1>(la, lb, st, kt + 1, nk, f0, f1, acc, arow0, nrow);
-    kstep<2>(la, lb, st, kt + 2, nk, f0, f1, acc, arow0, nrow);
-    kstep<3>(la, lb, st, kt + 3, nk, f0, f1, acc, arow0, nrow);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) read_frag<TA, TB>(f0, q, ring.a<0>(), ring.b<0>(), 0, arow0, nrow);
+  for (int j = 0; j < nk; j += kSlots) {
+    kstep<0>(la, lb, ring, j, nk, f0, f1, acc, arow0, nrow);
+    if (j + 1 < nk) kstep<1>(la, lb, ring, j + 1, nk, f0, f1, acc, arow0, nrow);
+    if (j + 2 < nk) kstep<2>(la, lb, ring, j + 2, nk, f0, f1, acc, arow0, nrow);
+    if (j + 3 < nk) kstep<3>(la, lb, ring, j + 3, nk, f0, f1, acc, arow0, nrow);
+    if (j + 4 < nk) kstep<4>(la, lb, ring, j + 4, nk, f0, f1, acc, arow0, nrow);
   }
   wait_loads<0>();
-  // every wave is past its last fragment read before the stages are reused
+  // every wave is past its last fragment read before the ring is reused
   __syncthreads();
 }
 
@@ -469,7 +462,7 @@ __global__ __launch_bounds__(256) void gemm_schedule(const int32_t* act, const i
 // ---------------------------------------------------------------------------
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1))) void ffn_gateup(FfnArgs a) {
-  MOONEP_STAGE_ARRAYS(smem);
+  MOONEP_RING(smem);
   int d, nt;
   Tile tl;
   if (!decode(a, &d, &tl, &nt)) return;
@@ -513,7 +506,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 // ---------------------------------------------------------------------------
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1))) void ffn_down(FfnArgs a) {
-  MOONEP_STAGE_ARRAYS(smem);
+  MOONEP_RING(smem);
   int d, nt;
   Tile tl;
   if (!decode(a, &d, &tl, &nt)) return;
@@ -563,7 +556,7 @@ struct WgradArgs {
 // Tile: 256 h (MFMA rows) x 256 h' (MFMA columns), contraction over t.
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1))) void wgrad_kernel(WgradArgs a) {
-  MOONEP_STAGE_ARRAYS(smem);
+  MOONEP_RING(smem);
   const int64_t lt = logical_tile();
   const int64_t total = (int64_t)a.nranks * a.L2 * a.ntm * a.ntn;
   if (lt >= total) return;
