@@ -235,9 +235,14 @@ __device__ __forceinline__ void read_frag(Frags& f, int q, const lds_t* A, const
   }
 }
 
+// acc[i][j] accumulates the 32x32 block (A rows arow0+32i.., B columns
+// nrow[j]..) transposed: the B fragment is the MFMA's first operand, so lane
+// (lr, lh) holds, in element v, output row arow0 + 32 i + lr and output column
+// nrow[j] + 8 (v/4) + 4 lh + v%4 -- four consecutive columns of one row per
+// v/4, which the epilogues store as one 8- or 16-byte piece.
 __device__ __forceinline__ void mma1(f32x16 acc[4][4], const Frags& f, int idx) {
   const int i = idx >> 2, j = idx & 3;
-  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
 // Wait until at most N LDS-DMA loads of this wave are outstanding.
@@ -353,8 +358,44 @@ __device__ __forceinline__ void zero_acc(f32x16 acc[4][4]) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 }
 
-// Row (within the 32x32 block) of accumulator element v of this lane.
-__device__ __forceinline__ int acc_row(int v, int lh) { return 8 * (v >> 2) + 4 * lh + (v & 3); }
+// Column (within the 32x32 block) of accumulator elements 4q..4q+3 of this
+// lane (the first of four consecutive columns).
+__device__ __forceinline__ int acc_col(int q, int lh) { return 8 * q + 4 * lh; }
+
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// Epilogue staging: a wave's bf16 output sub-tile (128 rows x NC columns) is
+// written to LDS row-major (8-byte pieces straight from the accumulator
+// layout), then read back 16 bytes per lane along whole rows and stored with
+// 16-byte buffer stores, so every store instruction writes complete rows.
+template <int NC>
+struct Stage {
+  static constexpr int kRowBytes = NC * 2 + 16;     // padded row (16-byte aligned)
+  static constexpr int kBytes = 128 * kRowBytes;
+  __device__ __forceinline__ static void put(lds_t* reg, int row, int col, unsigned lo, unsigned hi) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    *(__attribute__((address_space(3))) u32x2*)(reg + row * kRowBytes + col * 2) = u32x2{lo, hi};
+  }
+  // store the staged sub-tile: rows [0,128) to row m0 + r of `dst` (row
+  // stride ld elements, rows past the descriptor range dropped), columns
+  // [0,NC) to column c0 + c (columns at or past cols_valid dropped)
+  __device__ __forceinline__ static void flush(const lds_t* reg, Rsrc dst, int m0, int64_t ld,
+                                               int c0, int cols_valid) {
+    constexpr int kLanesPerRow = NC / 8, kRowsPerInst = 64 / kLanesPerRow;
+    const int lane = threadIdx.x & 63;
+    const int r0 = lane / kLanesPerRow, ch = lane % kLanesPerRow;
+    const int col = c0 + ch * 8;
+#pragma unroll
+    for (int t = 0; t < 128 / kRowsPerInst; ++t) {
+      const int r = t * kRowsPerInst + r0;
+      const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(reg + r * kRowBytes + ch * 16);
+      const uint32_t off = col < cols_valid ? (uint32_t)(((int64_t)(m0 + r) * ld + col) * 2) : kOob;
+      __builtin_amdgcn_raw_buffer_store_b128(v, dst, off, 0, 0);
+    }
+  }
+};
 
 // XCD-aware tile id: XCD x (= block id mod 8) walks the x-th contiguous
 // eighth of the logical tile range.
@@ -481,26 +522,31 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   zero_acc(acc);
   gemm_loop(la, lb, smem, a.H / BK, acc, wm * 128, nrow);
 
-  // SwiGLU epilogue: blocks j = 0,1 are gate, j = 2,3 the matching up.
+  // SwiGLU epilogue: blocks j = 0,1 are gate, j = 2,3 the matching up; the
+  // wave's 128 x 64 block of Z is staged in LDS and stored as whole rows.
   // Rows past the segment fall outside the store range; columns past H' get
   // an out-of-range offset.
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
-  const Rsrc zs = make_rsrc(a.z + ((int64_t)d * a.NvS + tl.m0) * a.Hp + n0,
-                            (int64_t)rows_valid * a.Hp * 2);
+  typedef Stage<64> St;
+  lds_t* reg = smem.base + wave * St::kBytes;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = wn * 64 + j * 32 + lr;
-      const uint32_t col = n < nvh ? (uint32_t)(n * 2) : kOob;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = wm * 128 + i * 32 + acc_row(v, lh);
-        const float g = acc[i][j][v], u = acc[i][j + 2][v];
-        const float zz = g / (1.0f + __expf(-g)) * u;
-        bstore16(zs, col + (uint32_t)(m * a.Hp * 2), bf16_rne(zz));
+      for (int q = 0; q < 4; ++q) {
+        float z[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float g = acc[i][j][4 * q + e], u = acc[i][j + 2][4 * q + e];
+          z[e] = g / (1.0f + __expf(-g)) * u;
+        }
+        St::put(reg, i * 32 + lr, j * 32 + acc_col(q, lh), pack_bf16x2(z[0], z[1]),
+                pack_bf16x2(z[2], z[3]));
       }
-    }
+  const Rsrc zs = make_rsrc(a.z + ((int64_t)d * a.NvS + tl.m0) * a.Hp + n0,
+                            (int64_t)rows_valid * a.Hp * 2);
+  St::flush(reg, zs, wm * 128, a.Hp, wn * 64, nvh);
 }
 
 // ---------------------------------------------------------------------------
@@ -524,20 +570,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   gemm_loop(la, lb, smem, a.Hp / BK, acc, wm * 128, nrow);
 
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
-  const Rsrc ys = make_rsrc(a.y + ((int64_t)d * a.NvS + tl.m0) * a.H + n0,
-                            (int64_t)rows_valid * a.H * 2);
+  typedef Stage<128> St;
+  lds_t* reg = smem.base + wave * St::kBytes;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = nrow[j] + lr;
-      const uint32_t col = n < cols_valid ? (uint32_t)(n * 2) : kOob;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = wm * 128 + i * 32 + acc_row(v, lh);
-        bstore16(ys, col + (uint32_t)(m * a.H * 2), bf16_rne(acc[i][j][v]));
-      }
-    }
+      for (int q = 0; q < 4; ++q)
+        St::put(reg, i * 32 + lr, j * 32 + acc_col(q, lh),
+                pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+  const Rsrc ys = make_rsrc(a.y + ((int64_t)d * a.NvS + tl.m0) * a.H + n0,
+                            (int64_t)rows_valid * a.H * 2);
+  St::flush(reg, ys, wm * 128, a.H, wn * 128, cols_valid);
 }
 
 // ---------------------------------------------------------------------------
@@ -586,27 +632,30 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   zero_acc(acc);
   gemm_loop(la, lb, smem, (ntok + BK - 1) / BK, acc, wm * 128, nrow);
 
-  // fp32 read-modify-write; rows past H and columns past H' are out of range
+  // fp32 read-modify-write, 4 consecutive columns (16 bytes) per access,
+  // masked to rows < H and columns < H'.  Plain global accesses: the 128-bit
+  // buffer-load builtin of this toolchain is lowered to a 32-bit load.
   const int64_t rs = (int64_t)a.H * a.Hp;
   float* G = (row < a.E ? a.gh + (int64_t)row * rs : a.rb + ((int64_t)d * a.B + row - a.E) * rs) +
              (int64_t)m0 * a.Hp + n0;
-  const Rsrc gs = make_rsrc(G, (int64_t)mv * a.Hp * 4);
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = nrow[j] + lr;
-      const uint32_t col = n < nv ? (uint32_t)(n * 4) : kOob;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = wm * 128 + i * 32 + acc_row(v, lh);
-        const uint32_t off = col + (uint32_t)(m * a.Hp * 4);
-        const float old = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gs, off, 0, 0));
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, __fadd_rn(old, acc[i][j][v])),
-                                              gs, off, 0, 0);
+      for (int q = 0; q < 4; ++q) {
+        const int m = wm * 128 + i * 32 + lr;
+        const int n = nrow[j] + acc_col(q, lh);
+        if (m < mv && n < nv) {
+          f32x4* gp = (f32x4*)(G + (int64_t)m * a.Hp + n);
+          f32x4 v = *gp;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = __fadd_rn(v[e], acc[i][j][4 * q + e]);
+          *gp = v;
+        }
       }
-    }
 }
 
 int64_t pad_grid(int64_t n) { return (n + kXcds - 1) / kXcds * kXcds; }
