@@ -426,11 +426,15 @@ __device__ __forceinline__ const uint16_t* weight_row(const FfnArgs& a, int p, i
   return row < a.E ? a.home[p] + (int64_t)row * rs : a.pool[p] + ((int64_t)d * a.B + row - a.E) * rs;
 }
 
-// Within a rank, tiles are taken in groups of kGroupM M-tiles: the group's
-// M-tiles for the first N-tile, then for the second, ...  Workgroups that run
-// together on an XCD (32 CUs) then cover kGroupM M-tiles x 32/kGroupM
-// N-tiles, so each weight slab in that XCD's L2 serves kGroupM workgroups and
-// each activation slab 32/kGroupM.
+// Within a rank, tiles are taken in groups of up to kGroupM M-tiles of one
+// segment (one expert): the group's M-tiles for the first N-tile, then for the
+// second, ...  Workgroups that run together on an XCD (32 CUs) then cover
+// kGroupM M-tiles x 32/kGroupM N-tiles of the same expert, so each weight
+// slab in that XCD's L2 serves the group's workgroups, and a group never
+// mixes two experts' weights.  Tile entry t holds (row, first slot, end slot,
+// group start * 16 + group size); the workgroups of a group starting at tile
+// g with size n are those with index l in [g ntn, (g + n) ntn), so l / ntn is
+// a tile of the same group and names it.
 constexpr int kGroupM = 4;
 
 __device__ __forceinline__ bool decode(const FfnArgs& a, int* d, Tile* tl, int* nt) {
@@ -440,13 +444,14 @@ __device__ __forceinline__ bool decode(const FfnArgs& a, int* d, Tile* tl, int* 
   if (lt >= total) return false;
   *d = a.rank0 + (int)(lt / per_rank);
   const int l = (int)(lt % per_rank);
-  const int group = l / (kGroupM * a.ntn);
-  const int gm = min(kGroupM, a.max_tiles - group * kGroupM);   // M-tiles in this group
-  const int rem = l - group * kGroupM * a.ntn;
+  const int tp = l / a.ntn;
+  if (tp >= a.ntiles[*d]) return false;
+  const int32_t* base = a.tiles + (int64_t)*d * a.max_tiles * 4;
+  const int grp = base[tp * 4 + 3];
+  const int gs = grp >> 4, gm = grp & 15;
+  const int rem = l - gs * a.ntn;
   *nt = rem / gm;
-  const int t = group * kGroupM + rem % gm;
-  if (t >= a.ntiles[*d]) return false;
-  const int32_t* e = a.tiles + ((int64_t)*d * a.max_tiles + t) * 4;
+  const int32_t* e = base + (gs + rem % gm) * 4;
   tl->row = e[0];
   tl->m0 = e[1];
   tl->m1 = e[2];
@@ -484,14 +489,17 @@ __global__ __launch_bounds__(256) void gemm_schedule(const int32_t* act, const i
     int before = 0;
     for (int i = 0; i < wv; ++i) before += wsum[i];
     if (tid == 255) s_total = before + x;
-    int t = base + before + x - n;
+    const int t0 = base + before + x - n;      // first tile of this segment
+    int t = t0;
     for (int m = end - len; m < end; m += BM, ++t) {
       if (t >= max_tiles) break;
       int32_t* e = tiles + ((int64_t)d * max_tiles + t) * 4;
+      const int gs = t0 + (t - t0) / kGroupM * kGroupM;
+      const int gm = min(kGroupM, t0 + n - gs);
       e[0] = row;
       e[1] = m;
       e[2] = m + BM < end ? m + BM : end;
-      e[3] = 0;
+      e[3] = gs * 16 + gm;
     }
     __syncthreads();
     base += s_total;
