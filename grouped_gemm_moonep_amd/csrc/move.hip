@@ -11,8 +11,9 @@
 //
 // Design for CDNA4: one wave per token row, 16-byte vector loads and stores
 // (64 lanes x 16 B = 1 KiB per instruction, fully coalesced), all loads of
-// a row chunk in flight before the stores, streaming (non-temporal) access
-// for data that is touched once.  Dispatch reads each token row once and
+// a row chunk in flight before the stores (combine: the K source rows of a
+// column vector in flight before the sum), non-temporal loads for data read
+// once.  Dispatch reads each token row once and
 // writes it K times (scatter); combine gathers K rows and writes one.  The
 // combine sum uses explicit round-to-nearest fp32 multiply and add
 // (__fmul_rn / __fadd_rn) in ascending k, so it is bit-reproducible.
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs a) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
           const int v = base + u * 64 + lane;
-          if (v < a.nv) __builtin_nontemporal_store(buf[u], dst + v);
+          if (v < a.nv) dst[v] = buf[u];
         }
       }
     }
@@ -111,7 +112,6 @@ struct CombineArgs {
   int ntok, K, nv;
 };
 
-constexpr int kCombineUnroll = 2;
 
 template <bool kWeighted>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
@@ -121,45 +121,39 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     const int tok = uniform(t);
     const int32_t* dk = a.dest + (int64_t)tok * a.K;
     u32x4* dst = a.out + (int64_t)tok * a.nv;
-    for (int base = 0; base < a.nv; base += 64 * kCombineUnroll) {
-      float acc[kCombineUnroll][8];
-      for (int k = 0; k < a.K; ++k) {
-        const int slot = uniform(dk[k]);
-        const u32x4* src = a.y + (int64_t)slot * a.nv;
-        float wk = 1.0f;
-        if (kWeighted) wk = a.rw_nvs[slot];
-        u32x4 yv[kCombineUnroll];
+    // the K source slots and weights of this token (wave-uniform)
+    int slots[kMaxK];
+    float wks[kMaxK];
+    for (int k = 0; k < a.K; ++k) {
+      slots[k] = uniform(dk[k]);
+      wks[k] = kWeighted ? a.rw_nvs[slots[k]] : 1.0f;
+    }
+    // per 16-byte column vector: up to 8 source rows in flight, then the sum
+    // in ascending k
+    for (int v = lane; v < a.nv; v += 64) {
+      float acc[8];
+      for (int k0 = 0; k0 < a.K; k0 += 8) {
+        const int kn = a.K - k0 < 8 ? a.K - k0 : 8;
+        u32x4 yv[8];
 #pragma unroll
-        for (int u = 0; u < kCombineUnroll; ++u) {
-          const int v = base + u * 64 + lane;
-          yv[u] = v < a.nv ? __builtin_nontemporal_load(src + v) : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int kk = 0; kk < 8; ++kk)
+          if (kk < kn) yv[kk] = __builtin_nontemporal_load(a.y + (int64_t)slots[k0 + kk] * a.nv + v);
 #pragma unroll
-        for (int u = 0; u < kCombineUnroll; ++u) {
-          float p[8];
+        for (int kk = 0; kk < 8; ++kk)
+          if (kk < kn) {
+            const int k = k0 + kk;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            p[2 * j] = bf16_lo(yv[u][j]);
-            p[2 * j + 1] = bf16_hi(yv[u][j]);
+            for (int j = 0; j < 8; ++j) {
+              const float pj0 = (j & 1) ? bf16_hi(yv[kk][j >> 1]) : bf16_lo(yv[kk][j >> 1]);
+              const float pj = kWeighted ? __fmul_rn(wks[k], pj0) : pj0;
+              acc[j] = (k == 0) ? pj : __fadd_rn(acc[j], pj);
+            }
           }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float pj = kWeighted ? __fmul_rn(wk, p[j]) : p[j];
-            acc[u][j] = (k == 0) ? pj : __fadd_rn(acc[u][j], pj);
-          }
-        }
       }
+      u32x4 o;
 #pragma unroll
-      for (int u = 0; u < kCombineUnroll; ++u) {
-        const int v = base + u * 64 + lane;
-        if (v < a.nv) {
-          u32x4 o;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            o[j] = bf16_rne(acc[u][2 * j]) | (bf16_rne(acc[u][2 * j + 1]) << 16);
-          __builtin_nontemporal_store(o, dst + v);
-        }
-      }
+      for (int j = 0; j < 4; ++j) o[j] = bf16_rne(acc[2 * j]) | (bf16_rne(acc[2 * j + 1]) << 16);
+      __builtin_nontemporal_store(o, dst + v);
     }
     if (kWeighted && a.rw_sk && lane < a.K)
       a.rw_sk[(int64_t)tok * a.K + lane] = a.rw_nvs[dk[lane]];
