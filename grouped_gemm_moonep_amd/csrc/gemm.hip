@@ -49,6 +49,7 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
 constexpr int BM = 256, BN = 256, BK = 64;        // K advances 64 per step
+constexpr int kHalfTileM = 128;                   // rows of a segment's short last tile
 constexpr int kXcds = 8;
 constexpr int kLoadsPerStep = 8;                  // LDS-DMA loads per wave per tile and step
 constexpr int kTileOffB = 0;                      // B tile offset inside its slot
@@ -136,8 +137,10 @@ __device__ __forceinline__ void bstore16(Rsrc r, uint32_t voff, unsigned v) {
 constexpr int kSlotBytes = 256 * BK * 2;          // 32 KiB
 constexpr int kSlots = 5;                         // 160 KiB ring
 
-struct RowTile {
+template <int NL>          // loads per wave per step: the tile has 32 NL rows
+struct RowTileT {
   static constexpr bool kRows = true;
+  static constexpr int kLoads = NL;
   DmaRsrc rs;
   uint32_t voff;        // this lane's offset for load 0 of k-block 0
   uint32_t step;        // byte distance between consecutive loads of a wave (8 rows)
@@ -146,20 +149,20 @@ struct RowTile {
   __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int rows_valid) {
     const int w = wave_id(), lane = threadIdx.x & 63;
     rs = make_dma_rsrc(base, (int64_t)rows_valid * ld * 2);
-    const int r = 64 * w + (lane >> 3);
+    const int r = 8 * NL * w + (lane >> 3);
     const int c = (lane & 7) ^ (r & 7);
     voff = (uint32_t)(r * ld * 2 + c * 16);
     step = (uint32_t)(16 * ld);
   }
   __device__ __forceinline__ uint32_t koff(int64_t k0) const { return (uint32_t)(k0 * 2); }
-  // load i (0..7) of this wave for the k-block at byte offset ko
+  // load i (0..NL-1) of this wave for the k-block at byte offset ko
   __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t ko, bool valid) const {
     const uint32_t s = __builtin_amdgcn_readfirstlane(valid ? ko + (uint32_t)i * step : kOob);
-    load_lds(rs, tile + (wave_id() * 8 + i) * 1024, voff + s);
+    load_lds(rs, tile + (wave_id() * NL + i) * 1024, voff + s);
   }
   __device__ __forceinline__ void issue(lds_t* tile, int64_t k0, bool valid) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) issue1(tile, i, koff(k0), valid);
+    for (int i = 0; i < NL; ++i) issue1(tile, i, koff(k0), valid);
   }
   // 8 consecutive k (sub-step kk of 4, lane half lh) of tile row `row`
   __device__ __forceinline__ static bf16x8 frag(const lds_t* tile, int row, int kk, int lh) {
@@ -167,9 +170,11 @@ struct RowTile {
     return *(const __attribute__((address_space(3))) bf16x8*)(tile + row * 128 + c * 16);
   }
 };
+typedef RowTileT<8> RowTile;      // 256 rows
 
 struct ColTile {
   static constexpr bool kRows = false;
+  static constexpr int kLoads = 8;
   DmaRsrc rs;           // this wave's region (waves 0,1: region 0; waves 2,3: region 1)
   uint32_t voff;        // this lane's offset for load 0 of k-block 0 (out of range past nv)
   uint32_t ld2;
@@ -212,25 +217,27 @@ struct ColTile {
   }
 };
 
-// MFMA fragments of one 16-deep sub-step for a wave: A rows arow0 + 32 i,
-// B columns nrow[j] (+ lane%32).
+// MFMA fragments of one 16-deep sub-step for a wave: A rows arow0 + 32 i
+// (i < MI), B columns nrow[j] (+ lane%32).
+template <int MI>
 struct Frags {
-  bf16x8 a[4], b[4];
+  bf16x8 a[MI], b[4];
 };
 
-// Fragment q of a sub-step, in the order the MFMAs consume them: A0, B0..B3,
-// A1..A3 (the MFMAs run i-major, so A0 and all of B are needed first).
-template <class TA, class TB>
-__device__ __forceinline__ void read_frag(Frags& f, int q, const lds_t* A, const lds_t* Bt,
+// Fragment q (< MI + 4) of a sub-step, in the order the MFMAs consume them:
+// A0, B0..B3, A1..A(MI-1) (the MFMAs run i-major, so A0 and all of B are
+// needed first).
+template <int MI, class TA, class TB>
+__device__ __forceinline__ void read_frag(Frags<MI>& f, int q, const lds_t* A, const lds_t* Bt,
                                           int kk, int arow0, const int nrow[4]) {
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
   if (q == 0 || q >= 5) {
     const int i = q == 0 ? 0 : q - 4;
-    f.a[i] = TA::kRows ? RowTile::frag(A, arow0 + i * 32 + lr, kk, lh)
+    f.a[i] = TA::kRows ? TA::frag(A, arow0 + i * 32 + lr, kk, lh)
                        : ColTile::frag(A, arow0 + i * 32, kk, lh);
   } else {
     const int j = q - 1;
-    f.b[j] = TB::kRows ? RowTile::frag(Bt, nrow[j] + lr, kk, lh)
+    f.b[j] = TB::kRows ? TB::frag(Bt, nrow[j] + lr, kk, lh)
                        : ColTile::frag(Bt, nrow[j], kk, lh);
   }
 }
@@ -240,7 +247,8 @@ __device__ __forceinline__ void read_frag(Frags& f, int q, const lds_t* A, const
 // (lr, lh) holds, in element v, output row arow0 + 32 i + lr and output column
 // nrow[j] + 8 (v/4) + 4 lh + v%4 -- four consecutive columns of one row per
 // v/4, which the epilogues store as one 8- or 16-byte piece.
-__device__ __forceinline__ void mma1(f32x16 acc[4][4], const Frags& f, int idx) {
+template <int MI>
+__device__ __forceinline__ void mma1(f32x16 acc[MI][4], const Frags<MI>& f, int idx) {
   const int i = idx >> 2, j = idx & 3;
   acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
@@ -279,23 +287,29 @@ struct Ring {
   __shared__ __attribute__((aligned(16))) char name##_[kSlots * kSlotBytes];       \
   const Ring name = {(lds_t*)name##_}
 
-// One 64-deep step j (J = j mod 5) = 64 MFMAs per wave in four 16-deep
-// sub-steps, with every other instruction slotted between MFMAs (an MFMA
-// occupies the matrix unit for 8 issue cycles of its wave):
+// One 64-deep step j (J = j mod 5) = 16 MI MFMAs per wave in four 16-deep
+// sub-steps of 4 MI, with every other instruction slotted between MFMAs (an
+// MFMA occupies the matrix unit for 8 issue cycles of its wave):
 //   sub-steps 0..2 read the next sub-step's fragments while computing;
-//   the 8 loads of A(j+1) go out after MFMAs 1, 4, ..., 22 and the 8 loads
-//   of B(j+2) after MFMAs 26, 30, ..., 54, one load per three or four MFMAs;
-//   after MFMA 55: wait for A(j+1) and B(j+1) (the 8 most recent loads are
-//   B(j+2)'s), wait for this wave's LDS reads, barrier;
-//   MFMAs 56..63 read step j+1's first fragments.
+//   the loads of A(j+1) go out after MFMAs 1, 4, 7, ... and then the 8 loads
+//   of B(j+2), spread over the rest of the step up to the barrier;
+//   after MFMA P-9 (P = 16 MI): wait for A(j+1) and B(j+1) (the 8 most
+//   recent loads are B(j+2)'s), wait for this wave's LDS reads, barrier;
+//   the last 8 MFMAs read step j+1's first fragments.
 // The barrier orders, for every wave, all reads of step j before any load
 // issued after it, and the arrival of step j+1's tiles before any read of
 // them.  A(j+2) then reuses B(j)'s slot and B(j+3) reuses A(j)'s.
-template <int J, class TA, class TB>
+template <int J, int MI, class TA, class TB>
 __device__ __forceinline__ void kstep(const TA& la, const TB& lb, const Ring& ring, int j, int nk,
-                                      Frags& f0, Frags& f1, f32x16 acc[4][4], int arow0,
+                                      Frags<MI>& f0, Frags<MI>& f1, f32x16 acc[MI][4], int arow0,
                                       const int nrow[4]) {
   constexpr int J1 = (J + 1) % kSlots, J2 = (J + 2) % kSlots;
+  constexpr int P = 16 * MI, SUB = 4 * MI, NF = MI + 4;
+  constexpr int NA = TA::kLoads, NB = TB::kLoads;
+  constexpr int BAR = P - 9;                       // barrier after this MFMA
+  constexpr int B0 = 3 * NA;                       // first B load position
+  constexpr int BS = (BAR - B0) / NB > 0 ? (BAR - B0) / NB : 1;
+  static_assert(B0 + BS * (NB - 1) <= BAR, "loads must precede the barrier");
   const lds_t* A = ring.a<J>();
   const lds_t* Bt = ring.b<J>();
   const lds_t* An = ring.a<J1>();
@@ -306,18 +320,19 @@ __device__ __forceinline__ void kstep(const TA& la, const TB& lb, const Ring& ri
   const bool va = j + 1 < nk, vb = j + 2 < nk;
   MOONEP_PIN();
 #pragma unroll
-  for (int p = 0; p < 64; ++p) {
-    const int sub = p >> 4, idx = p & 15;
-    mma1(acc, (sub & 1) ? f1 : f0, idx);
-    if (sub < 3 && idx < 8) read_frag<TA, TB>((sub & 1) ? f0 : f1, idx, A, Bt, sub + 1, arow0, nrow);
-    if (p % 3 == 1 && p <= 22) la.issue1(la_dst, p / 3, koa, va);
-    if (p >= 26 && p <= 54 && (p - 26) % 4 == 0) lb.issue1(lb_dst, (p - 26) / 4, kob, vb);
-    if (p == 55) {
+  for (int p = 0; p < P; ++p) {
+    const int sub = p / SUB, idx = p % SUB;
+    mma1<MI>(acc, (sub & 1) ? f1 : f0, idx);
+    if (sub < 3 && idx < NF)
+      read_frag<MI, TA, TB>((sub & 1) ? f0 : f1, idx, A, Bt, sub + 1, arow0, nrow);
+    if (p % 3 == 1 && p / 3 < NA) la.issue1(la_dst, p / 3, koa, va);
+    if (p >= B0 && (p - B0) % BS == 0 && (p - B0) / BS < NB) lb.issue1(lb_dst, (p - B0) / BS, kob, vb);
+    if (p == BAR) {
       MOONEP_PIN();
       wait_loads<kLoadsPerStep>();
       barrier_reads_done();
     }
-    if (p >= 56) read_frag<TA, TB>(f0, p - 56, An, Bn, 0, arow0, nrow);
+    if (p > BAR && p - BAR - 1 < NF) read_frag<MI, TA, TB>(f0, p - BAR - 1, An, Bn, 0, arow0, nrow);
     MOONEP_PIN();
   }
 }
@@ -325,33 +340,36 @@ __device__ __forceinline__ void kstep(const TA& la, const TB& lb, const Ring& ri
 // The K loop shared by every GEMM here.  The prologue loads B(0), A(0),
 // B(1); each step then loads A(j+1) and B(j+2) (out-of-range offsets past
 // the last step: they read nothing and keep the wait counts fixed).
-template <class TA, class TB>
+template <int MI, class TA, class TB>
 __device__ __forceinline__ void gemm_loop(const TA& la, const TB& lb, const Ring& ring, int nk,
-                                          f32x16 acc[4][4], int arow0, const int nrow[4]) {
+                                          f32x16 acc[MI][4], int arow0, const int nrow[4]) {
+  static_assert(TB::kLoads == kLoadsPerStep, "the barrier wait counts B loads");
   if (nk <= 0) return;
   lb.issue(ring.b<0>(), 0, true);
   la.issue(ring.a<0>(), 0, true);
   lb.issue(ring.b<1>(), BK, 1 < nk);
   wait_loads<kLoadsPerStep>();
   barrier_reads_done();
-  Frags f0, f1;
+  Frags<MI> f0, f1;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) read_frag<TA, TB>(f0, q, ring.a<0>(), ring.b<0>(), 0, arow0, nrow);
+  for (int q = 0; q < MI + 4; ++q)
+    read_frag<MI, TA, TB>(f0, q, ring.a<0>(), ring.b<0>(), 0, arow0, nrow);
   for (int j = 0; j < nk; j += kSlots) {
-    kstep<0>(la, lb, ring, j, nk, f0, f1, acc, arow0, nrow);
-    if (j + 1 < nk) kstep<1>(la, lb, ring, j + 1, nk, f0, f1, acc, arow0, nrow);
-    if (j + 2 < nk) kstep<2>(la, lb, ring, j + 2, nk, f0, f1, acc, arow0, nrow);
-    if (j + 3 < nk) kstep<3>(la, lb, ring, j + 3, nk, f0, f1, acc, arow0, nrow);
-    if (j + 4 < nk) kstep<4>(la, lb, ring, j + 4, nk, f0, f1, acc, arow0, nrow);
+    kstep<0, MI>(la, lb, ring, j, nk, f0, f1, acc, arow0, nrow);
+    if (j + 1 < nk) kstep<1, MI>(la, lb, ring, j + 1, nk, f0, f1, acc, arow0, nrow);
+    if (j + 2 < nk) kstep<2, MI>(la, lb, ring, j + 2, nk, f0, f1, acc, arow0, nrow);
+    if (j + 3 < nk) kstep<3, MI>(la, lb, ring, j + 3, nk, f0, f1, acc, arow0, nrow);
+    if (j + 4 < nk) kstep<4, MI>(la, lb, ring, j + 4, nk, f0, f1, acc, arow0, nrow);
   }
   wait_loads<0>();
   // every wave is past its last fragment read before the ring is reused
   __syncthreads();
 }
 
-__device__ __forceinline__ void zero_acc(f32x16 acc[4][4]) {
+template <int MI>
+__device__ __forceinline__ void zero_acc(f32x16 acc[MI][4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -366,19 +384,19 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
   return bf16_rne(lo) | (bf16_rne(hi) << 16);
 }
 
-// Epilogue staging: a wave's bf16 output sub-tile (128 rows x NC columns) is
+// Epilogue staging: a wave's bf16 output sub-tile (ROWS x NC columns) is
 // written to LDS row-major (8-byte pieces straight from the accumulator
 // layout), then read back 16 bytes per lane along whole rows and stored with
 // 16-byte buffer stores, so every store instruction writes complete rows.
-template <int NC>
+template <int ROWS, int NC>
 struct Stage {
   static constexpr int kRowBytes = NC * 2 + 16;     // padded row (16-byte aligned)
-  static constexpr int kBytes = 128 * kRowBytes;
+  static constexpr int kBytes = ROWS * kRowBytes;
   __device__ __forceinline__ static void put(lds_t* reg, int row, int col, unsigned lo, unsigned hi) {
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     *(__attribute__((address_space(3))) u32x2*)(reg + row * kRowBytes + col * 2) = u32x2{lo, hi};
   }
-  // store the staged sub-tile: rows [0,128) to row m0 + r of `dst` (row
+  // store the staged sub-tile: rows [0,ROWS) to row m0 + r of `dst` (row
   // stride ld elements, rows past the descriptor range dropped), columns
   // [0,NC) to column c0 + c (columns at or past cols_valid dropped)
   __device__ __forceinline__ static void flush(const lds_t* reg, Rsrc dst, int m0, int64_t ld,
@@ -388,7 +406,7 @@ struct Stage {
     const int r0 = lane / kLanesPerRow, ch = lane % kLanesPerRow;
     const int col = c0 + ch * 8;
 #pragma unroll
-    for (int t = 0; t < 128 / kRowsPerInst; ++t) {
+    for (int t = 0; t < ROWS / kRowsPerInst; ++t) {
       const int r = t * kRowsPerInst + r0;
       const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(reg + r * kRowBytes + ch * 16);
       const uint32_t off = col < cols_valid ? (uint32_t)(((int64_t)(m0 + r) * ld + col) * 2) : kOob;
@@ -509,36 +527,39 @@ __global__ __launch_bounds__(256) void gemm_schedule(const int32_t* act, const i
 }
 
 // ---------------------------------------------------------------------------
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(1, 1))) void ffn_gateup(FfnArgs a) {
-  MOONEP_RING(smem);
-  int d, nt;
-  Tile tl;
-  if (!decode(a, &d, &tl, &nt)) return;
+// Tile bodies, templated on MI = 32-row MFMA blocks per wave: MI = 4 is the
+// full 256-row tile (each wave 128 rows), MI = 2 the 128-row tile that ends a
+// segment whose padded length is an odd multiple of 128 (each wave 64 rows),
+// so a segment's last tile never computes 128 empty rows.
+
+// gate/up: 32 MI x 2 rows per workgroup, 128 gate + 128 up columns, K = H.
+template <int MI>
+__device__ __forceinline__ void gateup_tile(const FfnArgs& a, const Ring& smem, int d,
+                                            const Tile& tl, int nt) {
   const int n0 = nt * 128;
   const int rows_valid = tl.m1 - tl.m0;
   const int nvh = a.Hp - n0 < 128 ? a.Hp - n0 : 128;   // valid columns of each half
   const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int nrow[4] = {wn * 64, wn * 64 + 32, 128 + wn * 64, 128 + wn * 64 + 32};
 
-  RowTile la;
+  RowTileT<2 * MI> la;
   ColTile lb;
   la.init(a.x + ((int64_t)d * a.NvS + tl.m0) * a.H, a.H, rows_valid);
   lb.init(weight_row(a, 0, d, tl.row) + n0, weight_row(a, 1, d, tl.row) + n0, a.Hp, a.H, nvh,
           nvh);
-  f32x16 acc[4][4];
-  zero_acc(acc);
-  gemm_loop(la, lb, smem, a.H / BK, acc, wm * 128, nrow);
+  f32x16 acc[MI][4];
+  zero_acc<MI>(acc);
+  gemm_loop<MI>(la, lb, smem, a.H / BK, acc, wm * 32 * MI, nrow);
 
   // SwiGLU epilogue: blocks j = 0,1 are gate, j = 2,3 the matching up; the
-  // wave's 128 x 64 block of Z is staged in LDS and stored as whole rows.
+  // wave's 32 MI x 64 block of Z is staged in LDS and stored as whole rows.
   // Rows past the segment fall outside the store range; columns past H' get
   // an out-of-range offset.
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
-  typedef Stage<64> St;
+  typedef Stage<32 * MI, 64> St;
   lds_t* reg = smem.base + wave * St::kBytes;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -554,34 +575,32 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
       }
   const Rsrc zs = make_rsrc(a.z + ((int64_t)d * a.NvS + tl.m0) * a.Hp + n0,
                             (int64_t)rows_valid * a.Hp * 2);
-  St::flush(reg, zs, wm * 128, a.Hp, wn * 64, nvh);
+  St::flush(reg, zs, wm * 32 * MI, a.Hp, wn * 64, nvh);
 }
 
-// ---------------------------------------------------------------------------
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(1, 1))) void ffn_down(FfnArgs a) {
-  MOONEP_RING(smem);
-  int d, nt;
-  Tile tl;
-  if (!decode(a, &d, &tl, &nt)) return;
+// down: 32 MI x 2 rows per workgroup, 256 columns, K = H'.
+template <int MI>
+__device__ __forceinline__ void down_tile(const FfnArgs& a, const Ring& smem, int d,
+                                          const Tile& tl, int nt) {
   const int n0 = nt * BN;
   const int rows_valid = tl.m1 - tl.m0;
   const int cols_valid = a.H - n0 < BN ? a.H - n0 : BN;
   const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int nrow[4] = {wn * 128, wn * 128 + 32, wn * 128 + 64, wn * 128 + 96};
 
-  RowTile la, lb;
+  RowTileT<2 * MI> la;
+  RowTile lb;
   la.init(a.zin + ((int64_t)d * a.NvS + tl.m0) * a.Hp, a.Hp, rows_valid);
   lb.init(weight_row(a, 2, d, tl.row) + (int64_t)n0 * a.Hp, a.Hp, cols_valid);
-  f32x16 acc[4][4];
-  zero_acc(acc);
-  gemm_loop(la, lb, smem, a.Hp / BK, acc, wm * 128, nrow);
+  f32x16 acc[MI][4];
+  zero_acc<MI>(acc);
+  gemm_loop<MI>(la, lb, smem, a.Hp / BK, acc, wm * 32 * MI, nrow);
 
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
-  typedef Stage<128> St;
+  typedef Stage<32 * MI, 128> St;
   lds_t* reg = smem.base + wave * St::kBytes;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -591,7 +610,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                 pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
   const Rsrc ys = make_rsrc(a.y + ((int64_t)d * a.NvS + tl.m0) * a.H + n0,
                             (int64_t)rows_valid * a.H * 2);
-  St::flush(reg, ys, wm * 128, a.H, wn * 128, cols_valid);
+  St::flush(reg, ys, wm * 32 * MI, a.H, wn * 128, cols_valid);
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(1, 1))) void ffn_gateup(FfnArgs a) {
+  MOONEP_RING(smem);
+  int d, nt;
+  Tile tl;
+  if (!decode(a, &d, &tl, &nt)) return;
+  if (tl.m1 - tl.m0 <= kHalfTileM) gateup_tile<2>(a, smem, d, tl, nt);
+  else gateup_tile<4>(a, smem, d, tl, nt);
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(1, 1))) void ffn_down(FfnArgs a) {
+  MOONEP_RING(smem);
+  int d, nt;
+  Tile tl;
+  if (!decode(a, &d, &tl, &nt)) return;
+  if (tl.m1 - tl.m0 <= kHalfTileM) down_tile<2>(a, smem, d, tl, nt);
+  else down_tile<4>(a, smem, d, tl, nt);
 }
 
 // ---------------------------------------------------------------------------
@@ -637,8 +676,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   la.init(A, A + 128, a.H, ntok, mv0, mv1);
   lb.init(Bm, Bm + 128, a.Hp, ntok, nv0, nv1);
   f32x16 acc[4][4];
-  zero_acc(acc);
-  gemm_loop(la, lb, smem, (ntok + BK - 1) / BK, acc, wm * 128, nrow);
+  zero_acc<4>(acc);
+  gemm_loop<4>(la, lb, smem, (ntok + BK - 1) / BK, acc, wm * 128, nrow);
 
   // fp32 read-modify-write, 4 consecutive columns (16 bytes) per access,
   // masked to rows < H and columns < H'.  Plain global accesses: the 128-bit
