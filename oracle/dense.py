@@ -13,6 +13,12 @@ adds in ascending k, as the combine reading states.
 import numpy as np
 
 from .bf16 import bf16_to_f32, f32_to_bf16, f64_to_bf16
+from . import swiglu
+
+
+def _rnd_bf16(v):
+    """float64 -> nearest bf16 value (round to nearest even), as float64."""
+    return bf16_to_f32(f64_to_bf16(v)).astype(np.float64)
 
 
 def ffn_token(x_bits, wg_bits, wu_bits, wd_bits):
@@ -26,6 +32,16 @@ def ffn_token(x_bits, wg_bits, wu_bits, wd_bits):
     z = f64_to_bf16(g / (1.0 + np.exp(-g)) * u)
     y = f64_to_bf16(bf16_to_f32(z).astype(np.float64) @ wd.T)
     return z, y
+
+
+def ffn_token_backward(x_bits, dy_bits, wg_bits, wu_bits, wd_bits):
+    """Backward of one expert's SwiGLU for a batch of tokens [n,H] given the
+    gradient dy [n,H] of its output: returns (dz, dg, du, dx) bf16 bits, each
+    rounded where it is stored (see swiglu.backward)."""
+    f = lambda b: bf16_to_f32(b).astype(np.float64)
+    out = swiglu.backward(f(x_bits), f(dy_bits), f(wg_bits), f(wu_bits), f(wd_bits),
+                          rnd=_rnd_bf16)
+    return tuple(f64_to_bf16(v) for v in out)
 
 
 def dense_moe(topk, rw, x, home):

@@ -30,6 +30,7 @@ Readings where the pages are silent (each is also listed in the design notes):
 import numpy as np
 
 from .bf16 import bf16_to_f32, f32_to_bf16, f64_to_bf16
+from . import swiglu
 
 
 def _token_of(plan, t):
@@ -128,6 +129,31 @@ def expert_ffn(plan, x_nvs, home, pool, ranks=None):
             z[d, lo:hi] = Zb
             y[d, lo:hi] = f64_to_bf16(Y)
     return z, y
+
+
+def expert_ffn_backward(plan, x_nvs, dy_nvs, home, pool, ranks=None):
+    """Backward of the grouped SwiGLU over every segment (swiglu.backward,
+    stored tensors rounded to bf16): x_nvs, dy_nvs [R,NvS,H] bf16 bits ->
+    dz, dg, du [R,NvS,H'] and dx [R,NvS,H] bf16 bits, zero outside segments.
+    dy_nvs is the gradient of the loss w.r.t. the FFN output rows y_nvs."""
+    R, NvS = plan.R, plan.NvS
+    H = x_nvs.shape[-1]
+    Hp = home[0].shape[-1]
+    dz = np.zeros((R, NvS, Hp), dtype=np.uint16)
+    dg = np.zeros((R, NvS, Hp), dtype=np.uint16)
+    du = np.zeros((R, NvS, Hp), dtype=np.uint16)
+    dx = np.zeros((R, NvS, H), dtype=np.uint16)
+    rnd = lambda v: bf16_to_f32(f64_to_bf16(v)).astype(np.float64)
+    for d in (range(R) if ranks is None else ranks):
+        for row, lo, hi in _segments(plan, d):
+            X = bf16_to_f32(x_nvs[d, lo:hi]).astype(np.float64)
+            DY = bf16_to_f32(dy_nvs[d, lo:hi]).astype(np.float64)
+            wg, wu, wd = (bf16_to_f32(resolve_row(plan, d, row, home[p], pool[p]))
+                          .astype(np.float64) for p in range(3))
+            outs = swiglu.backward(X, DY, wg, wu, wd, rnd=rnd)
+            for tgt, v in zip((dz, dg, du, dx), outs):
+                tgt[d, lo:hi] = f64_to_bf16(v)
+    return dz, dg, du, dx
 
 
 def expert_wgrad(plan, a_nvs, b_nvs, grad_home, reduce_buf):
