@@ -193,6 +193,28 @@ class Buffer:
                                             _stream()), "moonep_expert_down")
         return y_nvs
 
+    def expert_ffn_bwd(self, plan, x_nvs, dy_nvs, home, pool, dz_ws=None, dg_nvs=None,
+                       du_nvs=None, dx_nvs=None, rank=-1):
+        """Backward of the grouped SwiGLU FFN: returns (dz_ws, dg_nvs, du_nvs,
+        dx_nvs); dx_nvs may be dy_nvs or x_nvs (in place)."""
+        R, NvS, H, Hp = self.R, self.NvS, self.H, self.Hp
+        dev = x_nvs.device
+        new = lambda W: torch.empty((R, NvS, W), dtype=torch.bfloat16, device=dev)
+        dz_ws = new(Hp) if dz_ws is None else dz_ws
+        dg_nvs = new(Hp) if dg_nvs is None else dg_nvs
+        du_nvs = new(Hp) if du_nvs is None else du_nvs
+        dx_nvs = new(H) if dx_nvs is None else dx_nvs
+        args = (int(rank), _dev_ptr(x_nvs, torch.bfloat16, (R, NvS, H), "x_nvs"),
+                _dev_ptr(dy_nvs, torch.bfloat16, (R, NvS, H), "dy_nvs"),
+                self._weights(home, False), self._weights(pool, True),
+                _dev_ptr(dz_ws, torch.bfloat16, (R, NvS, Hp), "dz_ws"),
+                _dev_ptr(dg_nvs, torch.bfloat16, (R, NvS, Hp), "dg_nvs"),
+                _dev_ptr(du_nvs, torch.bfloat16, (R, NvS, Hp), "du_nvs"),
+                _dev_ptr(dx_nvs, torch.bfloat16, (R, NvS, H), "dx_nvs"))
+        _abi.check(lib().moonep_expert_ffn_bwd(self._h, ctypes.byref(plan.struct), *args,
+                                               _stream()), "moonep_expert_ffn_bwd")
+        return dz_ws, dg_nvs, du_nvs, dx_nvs
+
     def expert_wgrad(self, plan, a_nvs, b_nvs, grad_home, reduce_buf, rank=-1):
         R, NvS, E, B, H, Hp = self.R, self.NvS, self.E, self.B, self.H, self.Hp
         args = (int(rank), _dev_ptr(a_nvs, torch.bfloat16, (R, NvS, H), "a_nvs"),

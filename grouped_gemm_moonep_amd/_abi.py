@@ -66,6 +66,8 @@ def lib():
         "moonep_expert_ffn": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, P3, P3, vp, vp, vp]),
         "moonep_expert_gateup": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, P3, P3, vp, vp]),
         "moonep_expert_down": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, P3, P3, vp, vp]),
+        "moonep_expert_ffn_bwd": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, vp, P3, P3, vp,
+                                        vp, vp, vp, vp]),
         "moonep_expert_wgrad": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, vp, vp, vp, vp]),
         "moonep_reduce_grad": (i32, [vp, ctypes.POINTER(MoonepPlan), P3, P3, vp]),
         "moonep_read_stats": (i32, [vp, ctypes.POINTER(MoonepPlan), vp, vp]),

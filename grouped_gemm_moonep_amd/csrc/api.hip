@@ -258,6 +258,30 @@ moonep_status_t moonep_expert_ffn(moonep_handle_t h, const moonep_plan_t* plan,
   return hip_status(e);
 }
 
+moonep_status_t moonep_expert_ffn_bwd(moonep_handle_t h, const moonep_plan_t* plan,
+                                      int32_t rank, const uint16_t* x_nvs,
+                                      const uint16_t* dy_nvs, const uint16_t* const home[3],
+                                      const uint16_t* const pool[3], uint16_t* dz_ws,
+                                      uint16_t* dg_nvs, uint16_t* du_nvs, uint16_t* dx_nvs,
+                                      hipStream_t stream) {
+  if (!h || !plan_ok(plan) || !x_nvs || !dy_nvs || !dz_ws || !dg_nvs || !du_nvs || !dx_nvs)
+    return MOONEP_ERR_ARG;
+  if (rank < -1 || rank >= h->c.d.R) return MOONEP_ERR_ARG;
+  const void* all[] = {x_nvs, dy_nvs, dz_ws, dg_nvs, du_nvs, dx_nvs};
+  for (const void* q : all)
+    if (!aligned(q, 16)) return MOONEP_ERR_ARG;
+  // dZ, dG and dU are distinct from each other and from every other buffer;
+  // dX may reuse the storage of dY or X (both are consumed before dX is written)
+  const void* ws[] = {dz_ws, dg_nvs, du_nvs};
+  const void* other[] = {x_nvs, dy_nvs, dx_nvs, dz_ws, dg_nvs, du_nvs};
+  for (int i = 0; i < 3; ++i)
+    for (int k = 0; k < 6; ++k)
+      if (ws[i] == other[k] && k != 3 + i) return MOONEP_ERR_ARG;
+  if (!weights_ok(h->c, home, pool, 0, 3)) return MOONEP_ERR_ARG;
+  return hip_status(launch_ffn_bwd(h->c, *plan, rank, x_nvs, dy_nvs, home, pool, dz_ws, dg_nvs,
+                                   du_nvs, dx_nvs, stream));
+}
+
 moonep_status_t moonep_expert_wgrad(moonep_handle_t h, const moonep_plan_t* plan,
                                     int32_t rank, const uint16_t* a_nvs,
                                     const uint16_t* b_nvs, float* grad_home,

@@ -77,6 +77,11 @@ hipError_t launch_gateup(const Ctx& c, const moonep_plan_t& p, int rank,
 hipError_t launch_down(const Ctx& c, const moonep_plan_t& p, int rank,
                        const uint16_t* z, const uint16_t* const home[3],
                        const uint16_t* const pool[3], uint16_t* y, hipStream_t s);
+hipError_t launch_ffn_bwd(const Ctx& c, const moonep_plan_t& p, int rank,
+                          const uint16_t* x, const uint16_t* dy,
+                          const uint16_t* const home[3], const uint16_t* const pool[3],
+                          uint16_t* dz, uint16_t* dg, uint16_t* du, uint16_t* dx,
+                          hipStream_t s);
 hipError_t launch_wgrad(const Ctx& c, const moonep_plan_t& p, int rank,
                         const uint16_t* a, const uint16_t* b, float* gh,
                         float* rb, hipStream_t s);

@@ -210,6 +210,30 @@ moonep_status_t moonep_expert_down(moonep_handle_t h, const moonep_plan_t* plan,
                                    const uint16_t* const pool[3],
                                    uint16_t* y_nvs, hipStream_t stream);
 
+/* Backward of the grouped SwiGLU FFN (the framework-side step between the
+ * README's "combine bwd" and "dispatch bwd"; derived from the forward of
+ * "Usage > Integration" by the chain rule).  For rank d (-1: all ranks) and
+ * every row i with cu_seqlens length > 0, over the row's padded segment:
+ *   dZ = bf16_rne(dY Wd_i)                        -> dz_ws  [R,NvS,Hp]
+ *   G = X Wg_i, U = X Wu_i recomputed (fp32), s = sigma(G),
+ *   dU = bf16_rne(dZ * G s)                       -> du_nvs [R,NvS,Hp]
+ *   dG = bf16_rne(dZ * U * s (1 + G (1 - s)))     -> dg_nvs [R,NvS,Hp]
+ *   dX = bf16_rne(dG Wg_i^T + dU Wu_i^T)          -> dx_nvs [R,NvS,H]
+ * x_nvs [R,NvS,H] is the forward input and dy_nvs [R,NvS,H] the gradient of
+ * the loss w.r.t. the FFN output rows y_nvs (a route-weighted loss scales it
+ * by rw_nvs first).  Weights resolve as in moonep_prefetch_weight.  dG and
+ * dU feed moonep_expert_wgrad (dWg = X^T dG, dWu = X^T dU); dWd = dY^T Z uses
+ * the forward's Z.  dx_nvs may equal x_nvs or dy_nvs; dz_ws, dg_nvs and
+ * du_nvs alias nothing.  Slots outside segments are not written. */
+moonep_status_t moonep_expert_ffn_bwd(moonep_handle_t h, const moonep_plan_t* plan,
+                                      int32_t rank, const uint16_t* x_nvs,
+                                      const uint16_t* dy_nvs,
+                                      const uint16_t* const home[3],
+                                      const uint16_t* const pool[3],
+                                      uint16_t* dz_ws, uint16_t* dg_nvs,
+                                      uint16_t* du_nvs, uint16_t* dx_nvs,
+                                      hipStream_t stream);
+
 /* Weight gradient of one projection (README "Gradient buffer"): for rank d
  * (-1: all) and every row i with length > 0, dW_i += A_seg^T B_seg in fp32,
  * A = a_nvs [R,NvS,H] bf16, B = b_nvs [R,NvS,Hp] bf16 (gate/up: A = x,

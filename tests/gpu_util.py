@@ -60,16 +60,18 @@ def bf16_ulp(want_bits):
     return nxt - mag
 
 
-def assert_close_bf16(got_bits, want_bits, rel=1e-2, abs_=2e-2, what=""):
+def assert_close_bf16(got_bits, want_bits, rel=1e-2, abs_=2e-2, what="", ulps=1):
     """GEMM/FFN tolerance: rel-L2 <= 1e-2 and, element-wise,
-    |got - want| <= max(2e-2, one bf16 ulp of want).  A bf16 output cannot be
-    closer to an independently rounded reference than one ulp of its own
-    grid, which exceeds 2e-2 once |want| >= 4."""
+    |got - want| <= max(2e-2, `ulps` bf16 ulps of want).  A bf16 output
+    cannot be closer to an independently rounded reference than one ulp of its
+    own grid, which exceeds 2e-2 once |want| >= 4; a value computed from
+    another rounded bf16 intermediate (the FFN backward) may sit one more ulp
+    away."""
     g = oracle.bf16_to_f32(got_bits).astype(np.float64)
     w = oracle.bf16_to_f32(want_bits).astype(np.float64)
     r = rel_l2(g, w)
     err = np.abs(g - w)
-    bound = np.maximum(abs_, bf16_ulp(want_bits))
+    bound = np.maximum(abs_, ulps * bf16_ulp(want_bits))
     m = float(err.max()) if g.size else 0.0
     worst = float((err / bound).max()) if g.size else 0.0
     assert r <= rel and worst <= 1.0, \

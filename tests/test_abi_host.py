@@ -91,6 +91,8 @@ def test_null_arguments_rejected_on_host():
                                     None) == ERR
     assert lib.moonep_expert_down(None, ctypes.byref(plan), -1, None, P3(), P3(), None,
                                   None) == ERR
+    assert lib.moonep_expert_ffn_bwd(None, ctypes.byref(plan), -1, None, None, P3(), P3(), None,
+                                     None, None, None, None) == ERR
     assert lib.moonep_expert_wgrad(None, ctypes.byref(plan), -1, None, None, None, None,
                                    None) == ERR
     assert lib.moonep_reduce_grad(None, ctypes.byref(plan), P3(), P3(), None) == ERR
