@@ -143,3 +143,67 @@ def test_ffn_bwd_full_size_sampled():
             assert_close_bf16(host_bf16(t[d, slots]), ref, what=f"{nm} d={d} row={row}",
                               ulps=1 if nm == "dz" else 2)
     buf.destroy()
+
+
+@pytest.mark.parametrize("name,target", [("tiny_r4_s64_k2_e8", 1.0), ("bwd_r8_s1024_k4_e32", 2.0)])
+def test_training_step_equals_dense(name, target):
+    """A whole training step of the MoE layer with an unweighted combine
+    (out = sum_k FFN_k(x)): forward, combine bwd (dispatch of dOut), FFN
+    backward, dispatch bwd (unweighted combine), weight gradients and
+    reduce_grad -- against a dense per-token computation that never sees a
+    plan: dx = sum_k dX_k (fp32, ascending k, bf16), dW_e = sum over the
+    tokens routed to e of the per-token weight gradients."""
+    w = synth.WORKLOADS[name]
+    log(f"training step {name} target={target}")
+    topk, _ = synth.routing(w, target)
+    x = synth.hidden(w)
+    dout = synth.grad_out(w, w.H)
+    home_h = [synth.expert_weights_host(w, i) for i in range(3)]
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    home = [dev_bf16(h) for h in home_h]
+    pool = [torch.zeros((w.R, w.B, w.H, w.Hp), dtype=torch.bfloat16, device="cuda")
+            for _ in range(3)]
+    buf.prefetch_weight(plan, home, pool)
+    x_nvs, _ = buf.dispatch(plan, dev_bf16(x))
+    z, y = buf.expert_ffn(plan, x_nvs, home, pool)
+    dy_nvs, _ = buf.dispatch(plan, dev_bf16(dout))                    # combine bwd
+    _, dg, du, dx_nvs = buf.expert_ffn_bwd(plan, x_nvs, dy_nvs, home, pool)
+    dx, _ = buf.combine(plan, dx_nvs)                                 # dispatch bwd
+    grads = [torch.zeros((w.E, w.H, w.Hp), dtype=torch.float32, device="cuda") for _ in range(3)]
+    rbuf = [torch.zeros((w.R, w.B, w.H, w.Hp), dtype=torch.float32, device="cuda")
+            for _ in range(3)]
+    buf.expert_wgrad(plan, x_nvs, dg, grads[0], rbuf[0])
+    buf.expert_wgrad(plan, x_nvs, du, grads[1], rbuf[1])
+    buf.expert_wgrad(plan, dy_nvs, z, grads[2], rbuf[2])
+    buf.reduce_grad(plan, grads, rbuf)
+    torch.cuda.synchronize()
+
+    # dense reference, token-major
+    R, S, K, E = w.R, w.S, w.K, w.E
+    xt = x.reshape(R * S, w.H)
+    dt = dout.reshape(R * S, w.H)
+    ids = topk.reshape(R * S, K)
+    dx_k = np.zeros((R * S, K, w.H), dtype=np.uint16)
+    f = lambda b: oracle.bf16_to_f32(b).astype(np.float64)
+    gw = [np.zeros((E, w.H, w.Hp)) for _ in range(3)]
+    for e in range(E):
+        t, k = np.nonzero(ids == e)
+        if t.size == 0:
+            continue
+        dz_e, dg_e, du_e, dx_e = oracle.ffn_token_backward(xt[t], dt[t], home_h[0][e],
+                                                           home_h[1][e], home_h[2][e])
+        z_e, _ = oracle.ffn_token(xt[t], home_h[0][e], home_h[1][e], home_h[2][e])
+        dx_k[t, k] = dx_e
+        gw[0][e] = f(xt[t]).T @ f(dg_e)
+        gw[1][e] = f(xt[t]).T @ f(du_e)
+        gw[2][e] = f(dt[t]).T @ f(z_e)
+    dx_want = oracle.combine_rows(dx_k).reshape(R, S, w.H)
+    assert_close_bf16(host_bf16(dx), dx_want, what="dx", ulps=2)
+    for i, nm in enumerate(("dWg", "dWu", "dWd")):
+        got = grads[i].cpu().numpy().astype(np.float64)
+        scale = max(np.abs(gw[i]).max(), 1.0)
+        err = np.abs(got - gw[i]).max() / scale
+        rel = np.linalg.norm(got - gw[i]) / max(np.linalg.norm(gw[i]), 1e-30)
+        assert rel <= 1e-2 and err <= 2e-2, f"{nm}: rel-L2 {rel:.2e}, max-abs/scale {err:.2e}"
+    buf.destroy()
