@@ -100,6 +100,74 @@ def cpu_baseline(w, topk, rw, width=512):
                         "combine": round(t3 - t2, 3)}}
 
 
+def time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool, steps, warmup):
+    """Backward of the step, timed per stage with HIP events on the launch
+    stream.  For each batch the forward inputs of the backward (plan, x_nvs,
+    prefetched weights, Z) are recomputed untimed; then: combine bwd (dispatch
+    of dOut), FFN backward (dZ, dG/dU, dX), dispatch bwd (unweighted combine
+    of dX), dW for gate, up and down, and reduce_grad."""
+    import torch
+    dev = x_nvs.device
+    g = torch.Generator(device=dev).manual_seed(1)
+    x = torch.randn((w.R, w.S, w.H), generator=g, device=dev).to(torch.bfloat16)
+    dout = torch.randn((w.R, w.S, w.H), generator=g, device=dev).to(torch.bfloat16)
+    dy_nvs = torch.empty_like(x_nvs)
+    dx_nvs = torch.empty_like(x_nvs)
+    dz, dg, du = (torch.empty_like(z_ws) for _ in range(3))
+    dx = torch.empty_like(x)
+    grads = [torch.zeros((w.E, w.H, w.Hp), dtype=torch.float32, device=dev) for _ in range(3)]
+    rbuf = [torch.zeros((w.R, w.B, w.H, w.Hp), dtype=torch.float32, device=dev) for _ in range(3)]
+    names = ["combine_bwd", "ffn_bwd", "dispatch_bwd", "wgrad_x3", "reduce_grad"]
+    per = {n: [] for n in names}
+    for i in range(warmup + steps):
+        _, topk, _ = batches[i % len(batches)]
+        buf.plan(topk, plan=plan)
+        buf.dispatch(plan, x, x_nvs=x_nvs)
+        buf.prefetch_weight(plan, home, pool)
+        buf.expert_gateup(plan, x_nvs, home, pool, z_ws)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record()
+        buf.dispatch(plan, dout, x_nvs=dy_nvs)
+        ev[1].record()
+        buf.expert_ffn_bwd(plan, x_nvs, dy_nvs, home, pool, dz, dg, du, dx_nvs)
+        ev[2].record()
+        buf.combine(plan, dx_nvs, out=dx)
+        ev[3].record()
+        buf.expert_wgrad(plan, x_nvs, dg, grads[0], rbuf[0])
+        buf.expert_wgrad(plan, x_nvs, du, grads[1], rbuf[1])
+        buf.expert_wgrad(plan, dy_nvs, z_ws, grads[2], rbuf[2])
+        ev[4].record()
+        buf.reduce_grad(plan, grads, rbuf)
+        ev[5].record()
+        torch.cuda.synchronize()
+        if i >= warmup:
+            for j, n in enumerate(names):
+                per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
+    slots = w.R * w.S * w.K
+    hh = float(w.H) * w.Hp
+    mean = {n: float(np.mean(v)) for n, v in per.items()}
+    out = {n + "_ms": round(t * 1e3, 3) for n, t in mean.items()}
+    out["ffn_bwd_TFLOPs"] = round(10 * hh * slots / mean["ffn_bwd"] / 1e12, 1)
+    out["wgrad_TFLOPs"] = round(6 * hh * slots / mean["wgrad_x3"] / 1e12, 1)
+    # weight gradients are HBM-bound: every gradient row (E home + R*B reduce
+    # slots, fp32) is read and written once per projection (accumulation),
+    # plus the bf16 operands of the three products
+    nvs_rows = w.R * buf.NvS
+    wgrad_bytes = 3 * (w.E + w.R * w.B) * hh * 4 * 2 + 2 * nvs_rows * (2 * w.H + 2 * w.Hp) \
+        + nvs_rows * (2 * w.H + 2 * w.Hp)
+    out["wgrad_GBps"] = round(wgrad_bytes / mean["wgrad_x3"] / 1e9, 1)
+    pb, db, cb = alg_bytes(w)
+    out["combine_bwd_GBps"] = round(db / mean["combine_bwd"] / 1e9, 1)
+    out["dispatch_bwd_GBps"] = round((slots * 2 * w.H + w.R * w.S * 2 * w.H + 4 * slots)
+                                     / mean["dispatch_bwd"] / 1e9, 1)
+    out["backward_ms"] = round(sum(mean.values()) * 1e3, 3)
+    out["note"] = ("flops per real slot: FFN backward 10 H H' (dZ 2, recomputed gate/up 4, "
+                   "dX 4), weight gradients 6 H H'; weight-gradient bytes: fp32 read-modify-"
+                   "write of every gradient row per projection plus the bf16 operands; steps "
+                   "cycle the same maxvio targets")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +175,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--targets", default="0,0.5,1,2,4,adv")
+    ap.add_argument("--train", action="store_true",
+                    help="also time a training step's backward (combine bwd, FFN backward, "
+                         "dispatch bwd, three weight gradients, reduce_grad) and report it "
+                         "under 'train'; needs ~90 GB more HBM for the fp32 gradient buffers")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before warmup, run torch.neg over a float32 buffer of MIB MiB "
                          "three times: a plain kernel of known traffic (reads and writes "
@@ -264,6 +336,9 @@ def main():
                              "traffic": None, "per_launch": {"bytes": cb, "avg_s": t_comb}},
         "sweep": sweep,
     }
+    if args.train:
+        result["train"] = time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool,
+                                        args.steps, args.warmup)
     buf.destroy()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
