@@ -14,6 +14,11 @@ kernel (the grouped FFN GEMM) and of dispatch/combine, and the CPU oracle
 timed on a bounded sample are reported alongside.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                    [--workload NAME] [--targets T,...] [--train]
+
+--workload pages_r8_s8192_k8_e384 times the shape of the pages' own benchmark
+(S=8192, E=384, maxvio 0.2/1/10/20); each sweep entry then also carries the
+pages' stacked "dispatch" (plan + prefetch + dispatch).
 """
 import argparse
 import json
@@ -174,7 +179,11 @@ def main():
     ap.add_argument("--steps", type=int, default=12)
     ap.add_argument("--warmup", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--targets", default="0,0.5,1,2,4,adv")
+    ap.add_argument("--workload", default=WORKLOAD, choices=sorted(synth.WORKLOADS),
+                    help="workload to time (default: the 8-rank S=4096 E=256 forward); "
+                         "pages_r8_s8192_k8_e384 is the shape of the pages' own benchmark")
+    ap.add_argument("--targets", default=None,
+                    help="comma-separated maxvio targets (default: the workload's sweep)")
     ap.add_argument("--train", action="store_true",
                     help="also time a training step's backward (combine bwd, FFN backward, "
                          "dispatch bwd, three weight gradients, reduce_grad) and report it "
@@ -192,10 +201,13 @@ def main():
     import torch
     from grouped_gemm_moonep_amd import Buffer
 
-    w = synth.WORKLOADS[WORKLOAD]
+    w = synth.WORKLOADS[args.workload]
     dev = "cuda"
-    targets = [t if t == "adv" else float(t) for t in args.targets.split(",")]
-    print(f"[bench] {WORKLOAD}: generating routing for {targets}", file=sys.stderr, flush=True)
+    if args.targets is None:
+        targets = list(synth.SWEEPS[args.workload])
+    else:
+        targets = [t if t == "adv" else float(t) for t in args.targets.split(",")]
+    print(f"[bench] {w.name}: generating routing for {targets}", file=sys.stderr, flush=True)
     batches = []
     host_routing = {}
     for t in targets:
@@ -301,8 +313,18 @@ def main():
             "gateup_ms": round(m("gateup") * 1e3, 3), "down_ms": round(m("down") * 1e3, 3),
             "combine_us": round(m("combine") * 1e6, 1),
             "pdc_GBps": round((pb + db + cb) / (m("plan") + m("dispatch") + m("combine")) / 1e9, 1),
+            "dispatch_stacked_us": round((m("plan") + m("prefetch") + m("dispatch")) * 1e6, 1),
             "gemm_TFLOPs": round(ffn_flops(w) / m("ffn") / 1e12, 1),
         }
+
+    # flatness (MoonEP README "Performance": time nearly flat in maxvio): each
+    # target's FFN and plan+dispatch+combine time over the lowest target's
+    keys = list(sweep)
+    if keys:
+        t0 = keys[0]
+        for k in keys:
+            sweep[k]["ffn_over_first"] = round(sweep[k]["ffn_ms"] / sweep[t0]["ffn_ms"], 3)
+            sweep[k]["pdc_over_first"] = round(sweep[t0]["pdc_GBps"] / sweep[k]["pdc_GBps"], 3)
 
     result = {
         "metric": "plan+dispatch+combine GB/s, grouped-GEMM TFLOP/s vs maxvio, 1 rank",
@@ -310,16 +332,17 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded Zipf-biased top-K routing, N(0,1) hidden, N(0,0.02) weights)",
-        "config": {"workload": WORKLOAD, "R": w.R, "S": w.S, "K": w.K, "E": w.E, "B": w.B,
+        "config": {"workload": w.name, "R": w.R, "S": w.S, "K": w.K, "E": w.E, "B": w.B,
                    "H": w.H, "Hp": w.Hp, "token_padding": w.token_padding,
                    "maxvio_targets": [str(t) for t in targets],
-                   "step": "plan, dispatch, prefetch_weight, expert_gateup + expert_down (8 ranks), combine"},
+                   "step": f"plan, dispatch, prefetch_weight, expert_gateup + expert_down "
+                           f"({w.R} ranks), combine"},
         "gemm_tflops": round(tflops, 1),
         "roofline": {"kernel": "ffn_gateup (gate and up GEMMs + SwiGLU, all 8 ranks, one launch)",
                      "bound": "mfma", "achieved": round(gateup_flops(w) / t_gu / 1e12, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gateup_flops(w) / t_gu / 1e12 / BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(),
+                     "traffic": measured_traffic() if w.name == WORKLOAD else None,
                      "per_launch": {"flops": gateup_flops(w), "avg_s": t_gu}},
         "roofline_down": {"kernel": "ffn_down (down GEMM, all 8 ranks, one launch)",
                           "bound": "mfma", "achieved": round(down_flops(w) / t_dn / 1e12, 1),

@@ -73,6 +73,10 @@ WORKLOADS = {
         # inference prefetch mode, B < E/R (README "How to set B": 3-4)
         Workload("infer_r8_s128_k8_e256_b4", R=8, S=128, K=8, E=256, B=4,
                  H=7168, Hp=2048, token_padding=128),
+        # the shape of the pages' own benchmark (README "Performance"): EP 8,
+        # S=8192, E=384, K=8, H=7168, H'=2048; training prefetch B = E/R
+        Workload("pages_r8_s8192_k8_e384", R=8, S=8192, K=8, E=384, B=48,
+                 H=7168, Hp=2048, token_padding=128),
     ]
 }
 # the training backward runs on the mid-size shapes
@@ -82,6 +86,7 @@ WORKLOADS["bwd_r8_s1024_k4_e32"] = dataclasses.replace(
 # imbalance targets swept per workload ("adv" = every token on experts 0..K-1)
 SWEEPS = {
     "tiny_r4_s64_k2_e8": [1.0],
+    "pages_r8_s8192_k8_e384": [0.2, 1.0, 10.0, 20.0],
     "mid_r8_s1024_k4_e32": [0.0, 0.5, 1.0, 2.0],
     "fwd_r8_s4096_k8_e256": [0.0, 0.5, 1.0, 2.0, 4.0, "adv"],
     "infer_r8_s128_k8_e256_b4": [1.0, 4.0],

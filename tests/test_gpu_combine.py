@@ -64,10 +64,12 @@ def test_dispatch_bwd_identity(target):
     buf.destroy()
 
 
-def test_combine_headline_sampled():
-    w = synth.WORKLOADS["fwd_r8_s4096_k8_e256"]
-    topk, _ = synth.routing(w, 4.0)
-    log("combine headline maxvio=4")
+@pytest.mark.parametrize("name,target", [("fwd_r8_s4096_k8_e256", 4.0),
+                                         ("pages_r8_s8192_k8_e384", 10.0)])
+def test_combine_full_size_sampled(name, target):
+    w = synth.WORKLOADS[name]
+    topk, _ = synth.routing(w, target)
+    log(f"combine {name} maxvio={target}")
     p = oracle.plan(topk, w.E, w.B, w.token_padding)
     g = torch.Generator(device="cuda").manual_seed(5)
     y = torch.randn((w.R, p.NvS, w.H), generator=g, device="cuda").to(torch.bfloat16)

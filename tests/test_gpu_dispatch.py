@@ -62,12 +62,15 @@ def test_dispatch_cu_budget():
     run(synth.WORKLOADS["mid_r8_s1024_k4_e32"], 1.0, num_cus=4)
 
 
-def test_dispatch_headline_sampled():
-    """Full size (4.7 GB of slots): every real slot checked through the
-    oracle's src map on a sample of slots; padding rows sampled for zeros."""
-    w = synth.WORKLOADS["fwd_r8_s4096_k8_e256"]
-    topk, rw = synth.routing(w, 2.0)
-    log("dispatch headline maxvio=2")
+@pytest.mark.parametrize("name,target", [("fwd_r8_s4096_k8_e256", 2.0),
+                                         ("pages_r8_s8192_k8_e384", 20.0)])
+def test_dispatch_full_size_sampled(name, target):
+    """Full size (4.7 GB of slots at the headline, 8.9 GB at the pages' shape):
+    sampled slots checked through the oracle's src map; padding rows sampled
+    for zeros."""
+    w = synth.WORKLOADS[name]
+    topk, rw = synth.routing(w, target)
+    log(f"dispatch {name} maxvio={target}")
     p = oracle.plan(topk, w.E, w.B, w.token_padding)
     g = torch.Generator(device="cuda").manual_seed(11)
     x = torch.randn((w.R, w.S, w.H), generator=g, device="cuda").to(torch.bfloat16)

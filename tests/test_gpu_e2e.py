@@ -141,7 +141,8 @@ def test_inference_overflow_forward():
 
 
 @pytest.mark.parametrize("name,target", [("fwd_r8_s4096_k8_e256", 2.0),
-                                         ("infer_r8_s128_k8_e256_b4", 4.0)])
+                                         ("infer_r8_s128_k8_e256_b4", 4.0),
+                                         ("pages_r8_s8192_k8_e384", 10.0)])
 def test_ffn_full_size_sampled(name, target):
     """Full-size weights drawn on the GPU; the oracle recomputes sampled rows
     of sampled segments token by token from the home weights."""

@@ -40,17 +40,21 @@ def run_and_compare(w, topk, tpe=None, full_check=True):
     return got
 
 
+FULL = ("fwd_", "pages_")
+
+
 @pytest.mark.parametrize("name,target", [
-    (n, t) for n, ts in synth.SWEEPS.items() for t in ts if not n.startswith("fwd_")])
+    (n, t) for n, ts in synth.SWEEPS.items() for t in ts if not n.startswith(FULL)])
 def test_plan_matches_oracle(name, target):
     w = synth.WORKLOADS[name]
     topk, _ = synth.routing(w, target)
     run_and_compare(w, topk)
 
 
-@pytest.mark.parametrize("target", synth.SWEEPS["fwd_r8_s4096_k8_e256"])
-def test_plan_matches_oracle_headline(target):
-    w = synth.WORKLOADS["fwd_r8_s4096_k8_e256"]
+@pytest.mark.parametrize("name,target", [
+    (n, t) for n, ts in synth.SWEEPS.items() for t in ts if n.startswith(FULL)])
+def test_plan_matches_oracle_full_size(name, target):
+    w = synth.WORKLOADS[name]
     topk, _ = synth.routing(w, target)
     run_and_compare(w, topk, full_check=False)
 
