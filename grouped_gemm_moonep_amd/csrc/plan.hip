@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   __shared__ int act_row[2 * kMaxE], act_end[2 * kMaxE], act_n[2 * kMaxE];
   __shared__ int nact[kMaxR], nrem[kMaxR], npf[kMaxR];
   __shared__ int hcount[kMaxE];
+  __shared__ int ord_len[3 * kMaxE], ord_ent[3 * kMaxE], ord_cnt[3 * kMaxE];  // phase F
   __shared__ int scan_scratch[32];
   __shared__ int s_err, s_maxload, s_ndon, s_dups, s_pad;
 
@@ -149,17 +150,17 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   __syncthreads();
 
   // Phase A: counts per (r, e) and exclusive per-chunk prefix (in place).
-  // Loads are batched 8 at a time so each thread keeps 8 in flight.
+  // Loads are batched 16 at a time so each thread keeps 16 in flight.
   for (int idx = tid; idx < RE; idx += kSolveThreads) {
     const int r = idx / E, e = idx - (idx / E) * E;
     int32_t* col = a.cc + (int64_t)r * nch * E + e;
     int run = 0;
-    for (int ch0 = 0; ch0 < nch; ch0 += 8) {
-      int v[8];
+    for (int ch0 = 0; ch0 < nch; ch0 += 16) {
+      int v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = ch0 + u < nch ? col[(int64_t)(ch0 + u) * E] : 0;
+      for (int u = 0; u < 16; ++u) v[u] = ch0 + u < nch ? col[(int64_t)(ch0 + u) * E] : 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 16; ++u)
         if (ch0 + u < nch) {
           col[(int64_t)(ch0 + u) * E] = run;
           run += v[u];
@@ -233,37 +234,42 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   }
   __syncthreads();
 
-  // Phase D: the serial chain-greedy (one thread, at most 2R iterations).
-  if (tid == 0) {
-    int nd = 0;
-    for (int g = 0; g < R; ++g) {
-      keep[g] = W[g] < C ? W[g] : C;
-      X[g] = W[g] - keep[g];
-      D[g] = C - keep[g];
-      need[g] = D[g];
-      recv_g[g] = -1;
-      recv_lo[g] = 0;
-      recv_hi[g] = 0;
-    }
-    // donors ordered by (-X, g)
-    for (int g = 0; g < R; ++g) {
-      if (X[g] <= 0) continue;
-      int pos = 0;
+  // Phase D: keep/excess/deficit per group, donors ordered by (-X, g) and
+  // receivers by (-D, r) (each group finds its own position), then the
+  // chain-greedy itself (one thread, at most 2R steps), then the line pieces
+  // of every group (one thread per group).
+  for (int g = tid; g < R; g += kSolveThreads) {
+    keep[g] = W[g] < C ? W[g] : C;
+    X[g] = W[g] - keep[g];
+    D[g] = C - keep[g];
+    need[g] = D[g];
+    recv_g[g] = -1;
+    recv_lo[g] = 0;
+    recv_hi[g] = 0;
+  }
+  __syncthreads();
+  for (int g = tid; g < R; g += kSolveThreads) {
+    int pos = 0;
+    if (X[g] > 0) {
       for (int h = 0; h < R; ++h)
         if (X[h] > 0 && (X[h] > X[g] || (X[h] == X[g] && h < g))) ++pos;
       donors[pos] = g;
-      ++nd;
     }
-    // receiver queue ordered by (-D, r)
-    int qh = 0, qt = 0;
-    for (int r = 0; r < R; ++r) {
-      if (D[r] <= 0) continue;
-      int pos = 0;
+    if (D[g] > 0) {
+      pos = 0;
       for (int h = 0; h < R; ++h)
-        if (D[h] > 0 && (D[h] > D[r] || (D[h] == D[r] && h < r))) ++pos;
-      queue[pos] = r;
-      ++qt;
+        if (D[h] > 0 && (D[h] > D[g] || (D[h] == D[g] && h < g))) ++pos;
+      queue[pos] = g;
     }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int nd = 0, qt = 0;
+    for (int g = 0; g < R; ++g) {
+      nd += X[g] > 0;
+      qt += D[g] > 0;
+    }
+    int qh = 0;
     int ndon = 0;
     int i = 0;
     int x = nd ? X[donors[0]] : 0;
@@ -287,28 +293,30 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
         x = i < nd ? X[donors[i]] : 0;
       }
     }
-    // pieces of every group's line: [0, keep) to the home rank, then the
-    // group's donations in emission order
-    for (int g = 0; g < R; ++g) {
-      int np = 0, lo = 0;
-      int32_t* pg = a.pieces + (int64_t)g * (R + 1) * 2;
-      if (keep[g] > 0) {
-        lo = keep[g];
-        pg[0] = lo; pg[1] = g; np = 1;
-      }
-      for (int q = 0; q < ndon; ++q) {
-        if (don_g[q] != g) continue;
-        don_lo[q] = lo;
-        lo += don_amt[q];
-        pg[2 * np] = lo; pg[2 * np + 1] = don_r[q]; ++np;
-        recv_g[don_r[q]] = g;
-        recv_lo[don_r[q]] = don_lo[q];
-        recv_hi[don_r[q]] = lo;
-      }
-      a.npieces[g] = np;
-    }
     s_ndon = ndon;
     if (bad) s_err = 8;   // internal: inconsistent counts (cannot happen)
+  }
+  __syncthreads();
+  // pieces of every group's line: [0, keep) to the home rank, then the
+  // group's donations in emission order
+  const int ndon_all = s_ndon;
+  for (int g = tid; g < R; g += kSolveThreads) {
+    int np = 0, lo = 0;
+    int32_t* pg = a.pieces + (int64_t)g * (R + 1) * 2;
+    if (keep[g] > 0) {
+      lo = keep[g];
+      pg[0] = lo; pg[1] = g; np = 1;
+    }
+    for (int q = 0; q < ndon_all; ++q) {
+      if (don_g[q] != g) continue;
+      const int dlo = lo;
+      lo += don_amt[q];
+      pg[2 * np] = lo; pg[2 * np + 1] = don_r[q]; ++np;
+      recv_g[don_r[q]] = g;        // each rank receives from at most one group
+      recv_lo[don_r[q]] = dlo;
+      recv_hi[don_r[q]] = lo;
+    }
+    a.npieces[g] = np;
   }
   __syncthreads();
 
@@ -353,71 +361,110 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   }
   __syncthreads();
 
-  // Phase F: walk each rank's active rows in ascending row order.
-  for (int d = tid; d < R; d += kSolveThreads) {
+  // Phase F: lay each rank's active rows out in ascending row order: the
+  // lower group's rows first (the rank's home experts or the remote experts
+  // that keep home rows), prefetch rows last.  Every active entry gets a
+  // visit-order slot (3L per rank); one block-wide scan over all slots gives
+  // each row's start and its index among the rank's active rows.
+  const int S3 = 3 * L;
+  const int nslot = R * S3;
+  for (int i = tid; i < nslot; i += kSolveThreads) {
+    ord_len[i] = 0;
+    ord_ent[i] = -1;
+  }
+  for (int d = tid; d < R; d += kSolveThreads) { nrem[d] = 0; npf[d] = 0; }
+  __syncthreads();
+  for (int idx = tid; idx < R * L2; idx += kSolveThreads) {
+    const int n = ent_n[idx];
+    if (n == 0) continue;
+    const int d = idx / L2, i = idx - (idx / L2) * L2;
     const int g = recv_g[d];
-    int q = 0, end = 0, rem = 0, pfc = 0, pad = 0;
-    // visit order: lower group's rows first, then prefetch rows by j
-    for (int pass = 0; pass < 3; ++pass) {
-      int base;   // entry offset of the block visited in this pass
-      bool home;
-      if (pass < 2) {
-        const bool home_first = g < 0 || d < g;
-        home = (pass == 0) == home_first;
-        base = home ? 0 : L;
-        if (!home && g < 0) continue;
-      } else {
-        home = false;
-        base = L;
-      }
-      for (int i = 0; i < L; ++i) {
-        const int idx = d * L2 + base + i;
-        const int n = ent_n[idx];
-        if (n == 0) continue;
-        const int row = ent_row[idx];
-        const bool is_pf = row >= E;
-        if (pass < 2 && is_pf) continue;          // prefetch rows come last
-        if (pass == 2 && !is_pf) continue;
-        const int len = round_up(n, a.tp);
-        end += len;
-        pad += len - n;
-        const int e = home ? d * L + i : g * L + i;
-        a.shift[d * E + e] = (end - len) - ent_lo[idx];
-        act_row[d * L2 + q] = row;
-        act_end[d * L2 + q] = end;
-        act_n[d * L2 + q] = n;
-        ++q;
-        if (!home && pass < 2) ++rem;
-        if (is_pf) {
-          a.pf[d * B + (row - E)] = e;
-          ++rem;
-          ++pfc;
-        }
-      }
-    }
-    nact[d] = q;
-    nrem[d] = rem;
-    npf[d] = pfc;
-    for (int j = pfc; j < B; ++j) a.pf[d * B + j] = -1;
-    for (int i = 0; i < L2; ++i) a.aux[a.ax.act + d * L2 + i] = i < q ? act_row[d * L2 + i] : -1;
-    a.stats[MOONEP_STAT_REMOTE_GROUP + d] = rem ? g : -1;
-    a.stats[MOONEP_STAT_REMOTE_GROUP + R + d] = rem;
-    atomicAdd(&s_dups, rem);
-    atomicAdd(&s_pad, pad);
+    const bool home_first = g < 0 || d < g;
+    int o;
+    if (i < L) o = (home_first ? 0 : L) + i;
+    else if (ent_row[idx] >= E) o = 2 * L + (i - L);
+    else o = (home_first ? L : 0) + (i - L);
+    ord_len[d * S3 + o] = round_up(n, a.tp);
+    ord_ent[d * S3 + o] = idx;
   }
   __syncthreads();
+  int tot_cnt;
+  {
+    const int per = (nslot + kSolveThreads - 1) / kSolveThreads;
+    const int b0 = min(nslot, tid * per), b1 = min(nslot, b0 + per);
+    int sl = 0, sc = 0;
+    for (int i = b0; i < b1; ++i) { sl += ord_len[i]; sc += ord_ent[i] >= 0; }
+    int tot_len;
+    int pl = block_exclusive_scan(sl, &tot_len, scan_scratch);
+    int pc = block_exclusive_scan(sc, &tot_cnt, scan_scratch);
+    for (int i = b0; i < b1; ++i) {          // exclusive prefixes, in place
+      const int l = ord_len[i];
+      ord_len[i] = pl;
+      ord_cnt[i] = pc;
+      pl += l;
+      pc += ord_ent[i] >= 0;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nslot; i += kSolveThreads) {
+    const int idx = ord_ent[i];
+    if (idx < 0) continue;
+    const int d = i / S3;
+    const int q = ord_cnt[i] - ord_cnt[d * S3];
+    const int start = ord_len[i] - ord_len[d * S3];
+    const int n = ent_n[idx];
+    const int len = round_up(n, a.tp);
+    const int row = ent_row[idx];
+    const int ie = idx - d * L2;
+    const bool home = ie < L;
+    const int e = home ? d * L + ie : recv_g[d] * L + (ie - L);
+    a.shift[d * E + e] = start - ent_lo[idx];
+    act_row[d * L2 + q] = row;
+    act_end[d * L2 + q] = start + len;
+    act_n[d * L2 + q] = n;
+    if (!home) atomicAdd(&nrem[d], 1);
+    if (row >= E) {
+      a.pf[d * B + (row - E)] = e;
+      atomicAdd(&npf[d], 1);
+    }
+    if (len > n) atomicAdd(&s_pad, len - n);
+  }
+  __syncthreads();
+  for (int d = tid; d < R; d += kSolveThreads) {
+    const int next = d + 1 < R ? ord_cnt[(d + 1) * S3] : tot_cnt;
+    nact[d] = next - ord_cnt[d * S3];
+    const int rem = nrem[d];
+    a.stats[MOONEP_STAT_REMOTE_GROUP + d] = rem ? recv_g[d] : -1;
+    a.stats[MOONEP_STAT_REMOTE_GROUP + R + d] = rem;
+    atomicAdd(&s_dups, rem);
+  }
+  __syncthreads();
+  for (int i = tid; i < R * B; i += kSolveThreads) {
+    const int d = i / B, j = i - (i / B) * B;
+    if (j >= npf[d]) a.pf[i] = -1;
+  }
+  for (int i = tid; i < R * L2; i += kSolveThreads) {
+    const int d = i / L2, q = i - (i / L2) * L2;
+    a.aux[a.ax.act + i] = q < nact[d] ? act_row[i] : -1;
+  }
 
   // Phase G: cu_seqlens and seg_tokens for every (rank, row).
   const int EB = E + B;
+  // The rank's active rows are in ascending row order: binary search for
+  // the last one at or below `row`.
   for (int idx = tid; idx < R * EB; idx += kSolveThreads) {
     const int d = idx / EB, row = idx - (idx / EB) * EB;
+    const int* ar = act_row + d * L2;
+    int lo = 0, hi = nact[d];          // first q with ar[q] > row lies in [lo, hi]
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (ar[mid] <= row) lo = mid + 1;
+      else hi = mid;
+    }
     int end = 0, n = 0;
-    const int na = nact[d];
-    for (int q = 0; q < na; ++q) {
-      const int rq = act_row[d * L2 + q];
-      if (rq > row) break;
-      end = act_end[d * L2 + q];
-      if (rq == row) n = act_n[d * L2 + q];
+    if (lo > 0) {
+      end = act_end[d * L2 + lo - 1];
+      if (ar[lo - 1] == row) n = act_n[d * L2 + lo - 1];
     }
     a.cu[idx] = end;
     a.segn[idx] = n;
@@ -462,27 +509,6 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     if (tid == 0) a.aux[a.ax.dup_n] = nexp;
   }
 
-  // Phase H: per-chunk line bases for plan_assign.
-  const int64_t ncc = (int64_t)R * nch * E;
-  for (int64_t i0 = tid; i0 < ncc; i0 += 8 * kSolveThreads) {
-    int v[8], w[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t idx = i0 + (int64_t)u * kSolveThreads;
-      if (idx < ncc) {
-        const int e = (int)(idx % E);
-        const int r = (int)(idx / ((int64_t)nch * E));
-        v[u] = a.cc[idx];
-        w[u] = aline[e] + a.rankpre[r * E + e];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t idx = i0 + (int64_t)u * kSolveThreads;
-      if (idx < ncc) a.cc[idx] = v[u] + w[u];
-    }
-  }
-
   if (tid == 0) {
     a.stats[MOONEP_STAT_ERROR] = s_err;
     a.stats[MOONEP_STAT_DUPS] = s_dups;
@@ -519,8 +545,11 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
   const bool tab = a.R * a.E <= kShiftLds && npc <= kPiecesLds;
   if (!err) {
     for (int i = tid; i < 4 * a.E; i += kPlanChunk) mask[i / a.E][i % a.E] = 0ull;
+    // line position of this chunk's first token of expert e: the expert's
+    // line start + tokens of lower ranks + tokens of earlier chunks of rank r
     const int32_t* gbase = a.cc + ((int64_t)r * a.nch + ch) * a.E;
-    for (int i = tid; i < a.E; i += kPlanChunk) s_base[i] = gbase[i];
+    for (int i = tid; i < a.E; i += kPlanChunk)
+      s_base[i] = gbase[i] + a.line[i] + a.rankpre[r * a.E + i];
     for (int i = tid; i < a.R; i += kPlanChunk) s_np[i] = a.npieces[i];
     if (tab) {
       for (int i = tid; i < a.R * a.E; i += kPlanChunk) s_shift[i] = a.shift[i];
