@@ -63,17 +63,22 @@ def down_flops(w):
 
 
 TRAFFIC_FILE = os.path.join(REPO, "profiles", "traffic_ffn_gateup_fwd_r8_s4096_k8_e256.txt")
-KERNEL_SOURCE = os.path.join(REPO, "grouped_gemm_moonep_amd", "csrc", "gemm.hip")
+KERNEL_SOURCES = [os.path.join(REPO, "grouped_gemm_moonep_amd", "csrc", f)
+                  for f in ("gemm_core.h", "gemm.hip")]
 
 
 def measured_traffic():
     """HBM bytes per ffn_gateup launch from the committed counter summary, or
-    None when the kernel source has changed since the counters were taken."""
+    None when the kernel's sources (gemm_core.h, gemm.hip) have changed since
+    the counters were taken."""
     import hashlib
     try:
         fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE)
                       if ":" in line and not line.startswith(" "))
-        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for f in KERNEL_SOURCES:
+            h.update(open(f, "rb").read())
+        src = h.hexdigest()
     except OSError:
         return None
     if fields.get("source_sha256", "").strip() != src:
