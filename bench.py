@@ -178,6 +178,91 @@ def time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool, steps, warmup)
     return out
 
 
+def time_overlap(w, batches, home, pool, steps, warmup, num_cus=32):
+    """Two micro-batches per step: communication calls (plan, dispatch,
+    prefetch, combine) on a second stream through a handle whose kernels are
+    capped at `num_cus` CUs (the README's num_sms budget), the FFN on the
+    compute stream; combine of A overlaps the FFN of B and dispatch of B the
+    FFN of A.  Reported beside the same two micro-batches run back to back."""
+    import torch
+    from grouped_gemm_moonep_amd import Buffer
+    dev = home[0].device
+    kw = dict(R=w.R, S=w.S, K=w.K, E=w.E, B=w.B, H=w.H, Hp=w.Hp, token_padding=w.token_padding)
+    comp = Buffer(**kw)
+    comm = Buffer(**kw, num_cus=num_cus)
+    g = torch.Generator(device=dev).manual_seed(2)
+    xs = [torch.randn((w.R, w.S, w.H), generator=g, device=dev).to(torch.bfloat16) for _ in range(2)]
+    plans = [comp.new_plan() for _ in range(2)]
+    x_nvs = [torch.empty((w.R, comp.NvS, w.H), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    rw_nvs = [torch.empty((w.R, comp.NvS), dtype=torch.float32, device=dev) for _ in range(2)]
+    z = torch.empty((w.R, comp.NvS, w.Hp), dtype=torch.bfloat16, device=dev)
+    outs = [torch.empty_like(xs[0]) for _ in range(2)]
+    pools = [pool, [torch.empty_like(t) for t in pool]]
+    s_comp = torch.cuda.current_stream()
+    s_comm = torch.cuda.Stream(device=dev)
+
+    def front(b, i, h):
+        _, topk, rw = batches[(2 * i + b) % len(batches)]
+        h.plan(topk, plan=plans[b])
+        h.dispatch(plans[b], xs[b], rw, x_nvs=x_nvs[b], rw_nvs=rw_nvs[b])
+        h.prefetch_weight(plans[b], home, pools[b])
+
+    def ffn(b):
+        comp.expert_gateup(plans[b], x_nvs[b], home, pools[b], z)
+        comp.expert_down(plans[b], z, home, pools[b], x_nvs[b])
+
+    def back(b, h):
+        h.combine(plans[b], x_nvs[b], rw_nvs[b], out=outs[b], gather_rw=False)
+
+    def serial(i):
+        for b in range(2):
+            front(b, i, comp)
+            ffn(b)
+            back(b, comp)
+
+    def overlapped(i):
+        ev = {k: torch.cuda.Event() for k in ("fa", "fb", "ffa", "ffb", "start")}
+        ev["start"].record(s_comp)
+        with torch.cuda.stream(s_comm):
+            s_comm.wait_event(ev["start"])
+            front(0, i, comm)
+            ev["fa"].record(s_comm)
+            front(1, i, comm)                 # overlaps the FFN of A
+            ev["fb"].record(s_comm)
+        s_comp.wait_event(ev["fa"])
+        ffn(0)
+        ev["ffa"].record(s_comp)
+        with torch.cuda.stream(s_comm):
+            s_comm.wait_event(ev["ffa"])
+            back(0, comm)                     # overlaps the FFN of B
+        s_comp.wait_event(ev["fb"])
+        ffn(1)
+        ev["ffb"].record(s_comp)
+        with torch.cuda.stream(s_comm):
+            s_comm.wait_event(ev["ffb"])
+            back(1, comm)
+        s_comp.wait_stream(s_comm)
+
+    res = {}
+    for name, fn in (("serial", serial), ("overlapped", overlapped)):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t0) / steps
+    comp.destroy()
+    comm.destroy()
+    return {"num_cus": num_cus, "micro_batches": 2,
+            "serial_ms": round(res["serial"] * 1e3, 3),
+            "overlapped_ms": round(res["overlapped"] * 1e3, 3),
+            "speedup": round(res["serial"] / res["overlapped"], 3),
+            "note": "ms per two micro-batches (plan, dispatch, prefetch, FFN, combine each); "
+                    "wall clock over the timed steps"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +278,9 @@ def main():
                     help="also time a training step's backward (combine bwd, FFN backward, "
                          "dispatch bwd, three weight gradients, reduce_grad) and report it "
                          "under 'train'; needs ~90 GB more HBM for the fp32 gradient buffers")
+    ap.add_argument("--overlap", action="store_true",
+                    help="also time two pipelined micro-batches with dispatch/combine on a "
+                         "second stream at a 32-CU budget against running them back to back")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before warmup, run torch.neg over a float32 buffer of MIB MiB "
                          "three times: a plain kernel of known traffic (reads and writes "
@@ -364,6 +452,33 @@ def main():
                              "traffic": None, "per_launch": {"bytes": cb, "avg_s": t_comb}},
         "sweep": sweep,
     }
+    # the copy that zero-copy avoids (README "API guide > zero_copy"): copy
+    # mode adds one copy of the used slots to dispatch and one to combine
+    t_last, topk_last, _ = batches[-1]
+    buf.plan(topk_last, plan=plan)
+    scratch = torch.empty_like(x_nvs)
+    for _ in range(2):
+        buf.copy_rows(plan, x_nvs, scratch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        buf.copy_rows(plan, x_nvs, scratch)
+    e1.record()
+    torch.cuda.synchronize()
+    t_copy = e0.elapsed_time(e1) / 5 * 1e-3
+    used = int(buf.read_stats(plan)[4]) + w.R * w.S * w.K          # padding + real rows
+    result["copy_mode"] = {
+        "copy_rows_us": round(t_copy * 1e6, 1),
+        "copy_rows_GBps": round(2 * 2 * w.H * used / t_copy / 1e9, 1),
+        "dispatch_us_copy_mode": round((t_disp + t_copy) * 1e6, 1),
+        "combine_us_copy_mode": round((t_comb + t_copy) * 1e6, 1),
+        "note": f"one copy of the used slots (real + padding rows) per call, timed at maxvio {t_last}"}
+    del scratch
+
+    if args.overlap:
+        result["overlap"] = time_overlap(w, batches, home, pool, max(2, args.steps // 2),
+                                         max(1, args.warmup // 2))
+
     if args.train:
         result["train"] = time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool,
                                         args.steps, args.warmup)

@@ -110,7 +110,33 @@ class Buffer:
                    "moonep_plan")
         return plan
 
-    def dispatch(self, plan, x, rw=None, x_nvs=None, rw_nvs=None):
+    def copy_rows(self, plan, src_nvs, dst_nvs=None):
+        """The used slots of every rank from src_nvs to dst_nvs (moonep_copy_rows)."""
+        R, NvS = self.R, self.NvS
+        W = src_nvs.shape[-1]
+        if dst_nvs is None:
+            dst_nvs = torch.empty_like(src_nvs)
+        args = (_dev_ptr(src_nvs, torch.bfloat16, (R, NvS, W), "src_nvs"), int(W),
+                _dev_ptr(dst_nvs, torch.bfloat16, (R, NvS, W), "dst_nvs"))
+        _abi.check(lib().moonep_copy_rows(self._h, ctypes.byref(plan.struct), *args, _stream()),
+                   "moonep_copy_rows")
+        return dst_nvs
+
+    def _comm(self, W, device):
+        """The communication buffer of the copy mode (zero_copy=False), one per
+        row width, owned by this Buffer."""
+        bufs = self.__dict__.setdefault("_comm_bufs", {})
+        if W not in bufs:
+            bufs[W] = torch.empty((self.R, self.NvS, W), dtype=torch.bfloat16, device=device)
+        return bufs[W]
+
+    def dispatch(self, plan, x, rw=None, x_nvs=None, rw_nvs=None, zero_copy=True):
+        """zero_copy=False (the README's copy mode): dispatch into this Buffer's
+        communication buffer, then copy the used slots into x_nvs."""
+        if not zero_copy:
+            comm, rw_nvs = self.dispatch(plan, x, rw, x_nvs=self._comm(x.shape[-1], x.device),
+                                         rw_nvs=rw_nvs)
+            return self.copy_rows(plan, comm, x_nvs), rw_nvs
         R, S, K, NvS = self.R, self.S, self.K, self.NvS
         W = x.shape[-1]
         if x_nvs is None:
@@ -125,7 +151,13 @@ class Buffer:
                    "moonep_dispatch")
         return x_nvs, rw_nvs
 
-    def combine(self, plan, y_nvs, rw_nvs=None, out=None, rw_sk=None, gather_rw=True):
+    def combine(self, plan, y_nvs, rw_nvs=None, out=None, rw_sk=None, gather_rw=True,
+                zero_copy=True):
+        """zero_copy=False (the README's copy mode): copy the used slots of
+        y_nvs into this Buffer's communication buffer first, then combine."""
+        if not zero_copy:
+            comm = self.copy_rows(plan, y_nvs, self._comm(y_nvs.shape[-1], y_nvs.device))
+            return self.combine(plan, comm, rw_nvs, out, rw_sk, gather_rw)
         R, S, K, NvS = self.R, self.S, self.K, self.NvS
         W = y_nvs.shape[-1]
         if out is None:

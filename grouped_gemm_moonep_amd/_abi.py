@@ -62,6 +62,7 @@ def lib():
         "moonep_plan": (i32, [vp, vp, vp, ctypes.POINTER(MoonepPlan), vp]),
         "moonep_dispatch": (i32, [vp, ctypes.POINTER(MoonepPlan), vp, i32, vp, vp, vp, vp]),
         "moonep_combine": (i32, [vp, ctypes.POINTER(MoonepPlan), vp, i32, vp, vp, vp, vp]),
+        "moonep_copy_rows": (i32, [vp, ctypes.POINTER(MoonepPlan), vp, i32, vp, vp]),
         "moonep_prefetch_weight": (i32, [vp, ctypes.POINTER(MoonepPlan), P3, P3, vp]),
         "moonep_expert_ffn": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, P3, P3, vp, vp, vp]),
         "moonep_expert_gateup": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, P3, P3, vp, vp]),

@@ -195,6 +195,15 @@ moonep_status_t moonep_combine(moonep_handle_t h, const moonep_plan_t* plan,
   return hip_status(launch_combine(h->c, *plan, y_nvs, W, rw_nvs, out, rw_sk, stream));
 }
 
+moonep_status_t moonep_copy_rows(moonep_handle_t h, const moonep_plan_t* plan,
+                                 const uint16_t* src_nvs, int32_t W, uint16_t* dst_nvs,
+                                 hipStream_t stream) {
+  if (!h || !plan_ok(plan) || !src_nvs || !dst_nvs) return MOONEP_ERR_ARG;
+  if (W <= 0 || W % 8 || !aligned(src_nvs, 16) || !aligned(dst_nvs, 16)) return MOONEP_ERR_ARG;
+  if ((const void*)src_nvs == (const void*)dst_nvs) return MOONEP_ERR_ARG;
+  return hip_status(launch_copy_rows(h->c, *plan, src_nvs, W, dst_nvs, stream));
+}
+
 moonep_status_t moonep_prefetch_weight(moonep_handle_t h, const moonep_plan_t* plan,
                                        const uint16_t* const home[3],
                                        uint16_t* const pool[3], hipStream_t stream) {

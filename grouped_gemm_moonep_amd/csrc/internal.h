@@ -64,6 +64,9 @@ hipError_t launch_dispatch(const Ctx& c, const moonep_plan_t& p,
 hipError_t launch_combine(const Ctx& c, const moonep_plan_t& p,
                           const uint16_t* y, int W, const float* rw_nvs,
                           uint16_t* out, float* rw_sk, hipStream_t s);
+hipError_t launch_copy_rows(const Ctx& c, const moonep_plan_t& p,
+                            const uint16_t* src, int W, uint16_t* dst,
+                            hipStream_t s);
 hipError_t launch_prefetch(const Ctx& c, const moonep_plan_t& p,
                            const uint16_t* const home[3],
                            uint16_t* const pool[3], hipStream_t s);

@@ -239,6 +239,42 @@ __global__ __launch_bounds__(kThreads) void reduce_grad_kernel(ReduceArgs a) {
   }
 }
 
+// copy_rows: the used slots of every rank (rows [0, cu_seqlens[d][E+B-1]),
+// padding rows included) from one [R,NvS,W] buffer to another; 16-byte
+// vectors, grid-stride over (rank, row).
+struct CopyArgs {
+  const u32x4* src;
+  u32x4* dst;
+  const int32_t* cu;     // [R][E+B]
+  int R, EB, nv, NvS;
+};
+
+__global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int64_t rows = (int64_t)a.R * a.NvS;
+  for (int64_t g = (int64_t)blockIdx.x * kWaves + wv; g < rows; g += (int64_t)gridDim.x * kWaves) {
+    const int d = (int)(g / a.NvS);
+    const int i = (int)(g - (int64_t)d * a.NvS);
+    if (i >= a.cu[d * a.EB + a.EB - 1]) continue;
+    const u32x4* s = a.src + g * a.nv;
+    u32x4* t = a.dst + g * a.nv;
+    for (int v0 = 0; v0 < a.nv; v0 += 64 * kUnroll) {
+      u32x4 buf[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int v = v0 + u * 64 + lane;
+        if (v < a.nv) buf[u] = __builtin_nontemporal_load(s + v);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int v = v0 + u * 64 + lane;
+        if (v < a.nv) t[v] = buf[u];
+      }
+    }
+  }
+}
+
 int capped_grid(const Ctx& c, int64_t want) {
   int64_t cap = want;
   if (c.d.num_cus > 0) cap = (int64_t)c.d.num_cus * 8;
@@ -275,6 +311,17 @@ hipError_t launch_combine(const Ctx& c, const moonep_plan_t& p, const uint16_t* 
     combine_kernel<true><<<blocks, kThreads, 0, s>>>(a);
   else
     combine_kernel<false><<<blocks, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const Ctx& c, const moonep_plan_t& p, const uint16_t* src, int W,
+                            uint16_t* dst, hipStream_t s) {
+  const Dims& d = c.d;
+  CopyArgs a;
+  a.src = (const u32x4*)src; a.dst = (u32x4*)dst; a.cu = p.cu_seqlens;
+  a.R = d.R; a.EB = d.E + d.B; a.nv = W / 8; a.NvS = (int)d.NvS;
+  const int blocks = capped_grid(c, ((int64_t)d.R * d.NvS + kWaves - 1) / kWaves);
+  copy_rows_kernel<<<blocks, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

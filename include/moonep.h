@@ -161,6 +161,16 @@ moonep_status_t moonep_combine(moonep_handle_t h, const moonep_plan_t* plan,
                                const float* rw_nvs, uint16_t* out,
                                float* rw_sk, hipStream_t stream);
 
+/* Copy of the used slots (README "API guide > zero_copy"): with zero_copy
+ * off, dispatch hands back a new tensor copied out of the communication
+ * buffer, and combine first copies its input into that buffer.  This call is
+ * that copy: for every rank d, rows [0, cu_seqlens[d][E+B-1]) of src_nvs
+ * [R,NvS,W] bf16 (padding rows included) are copied to dst_nvs; the rows past
+ * the last segment are not touched.  W % 8 == 0; src and dst must differ. */
+moonep_status_t moonep_copy_rows(moonep_handle_t h, const moonep_plan_t* plan,
+                                 const uint16_t* src_nvs, int32_t W,
+                                 uint16_t* dst_nvs, hipStream_t stream);
+
 /* Prefetch (README "API guide > dispatch fwd", prefetch_weight; "Weight
  * buffer").  home[p] [E,H,Hp] bf16 for p = gate, up, down; pool[p]
  * [R,B,H,Hp]: pool[p][d][j] becomes a bit copy of home[p][prefetch_src[d][j]]

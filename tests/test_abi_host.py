@@ -84,6 +84,7 @@ def test_null_arguments_rejected_on_host():
     assert lib.moonep_plan(None, None, None, ctypes.byref(plan), None) == ERR
     assert lib.moonep_dispatch(None, ctypes.byref(plan), None, 8, None, None, None, None) == ERR
     assert lib.moonep_combine(None, ctypes.byref(plan), None, 8, None, None, None, None) == ERR
+    assert lib.moonep_copy_rows(None, ctypes.byref(plan), None, 8, None, None) == ERR
     assert lib.moonep_prefetch_weight(None, ctypes.byref(plan), P3(), P3(), None) == ERR
     assert lib.moonep_expert_ffn(None, ctypes.byref(plan), -1, None, P3(), P3(), None, None,
                                  None) == ERR

@@ -92,3 +92,30 @@ def test_dispatch_full_size_sampled(name, target):
     grw = rw_nvs.cpu().numpy()
     assert np.array_equal(grw[d[real], slot[real]], rw.reshape(-1)[src[real]])
     buf.destroy()
+
+
+@pytest.mark.parametrize("target", [1.0, "adv"])
+def test_copy_mode_equals_zero_copy(target):
+    """zero_copy=False (README "API guide > zero_copy"): dispatch into the
+    Buffer's communication buffer and copy the used slots out; combine copies
+    its input in first.  Same bits as the zero-copy calls on every used slot;
+    rows past the last segment of the destination are left alone."""
+    w = synth.WORKLOADS["mid_r8_s1024_k4_e32"]
+    topk, rw = synth.routing(w, target)
+    p = oracle.plan(topk, w.E, w.B, w.token_padding)
+    x = dev_bf16(synth.hidden(w))
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    a, ra = buf.dispatch(plan, x, dev(rw))
+    b = torch.full((w.R, buf.NvS, w.H), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    b, rb = buf.dispatch(plan, x, dev(rw), x_nvs=b, zero_copy=False)
+    ah, bh = host_bf16(a), host_bf16(b)
+    for d in range(w.R):
+        end = p.cu_seqlens[d, -1]
+        assert np.array_equal(ah[d, :end], bh[d, :end])
+        assert (bh[d, end:] == SENTINEL).all()
+    assert torch.equal(ra, rb)
+    o1, g1 = buf.combine(plan, a, ra)
+    o2, g2 = buf.combine(plan, b, rb, zero_copy=False)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(g1, g2)
+    buf.destroy()
