@@ -263,6 +263,60 @@ def time_overlap(w, batches, home, pool, steps, warmup, num_cus=32):
                     "wall clock over the timed steps"}
 
 
+def time_views(w, buf, batches, home, pool, x, steps):
+    """The FFN and prefetch over per-rank [E+B,H,H'] views on virtual memory
+    (SymmetricBuffer: every rank's view maps the same home chunks) beside the
+    same calls over ordinary home / pool tensors, on the same plans and
+    inputs, alternating step by step."""
+    import torch
+    from grouped_gemm_moonep_amd import SymmetricBuffer
+    sbs = [SymmetricBuffer(buf) for _ in range(3)]
+    for i, sb in enumerate(sbs):
+        sb.home.copy_(home[i])
+    views = [sb.views for sb in sbs]
+    dev = x.device
+    plan = buf.new_plan()
+    x_nvs = torch.empty((w.R, buf.NvS, w.H), dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x_nvs)
+    z = torch.empty((w.R, buf.NvS, w.Hp), dtype=torch.bfloat16, device=dev)
+    t = {"prefetch_views": [], "ffn_views": [], "prefetch_split": [], "ffn_split": []}
+    for i in range(steps + 1):
+        _, topk, rw = batches[i % len(batches)]
+        buf.plan(topk, plan=plan)
+        buf.dispatch(plan, x, rw, x_nvs=x_nvs)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record()
+        buf.prefetch_weight_views(plan, views)
+        ev[1].record()
+        buf.expert_ffn_views(plan, x_nvs, views, z_ws=z, y_nvs=y)
+        ev[2].record()
+        ev[3].record()
+        buf.prefetch_weight(plan, home, pool)
+        ev[4].record()
+        buf.expert_ffn(plan, x_nvs, home, pool, z_ws=z, y_nvs=y)
+        ev[5].record()
+        torch.cuda.synchronize()
+        if i == 0:
+            continue                          # first pass warms both paths
+        t["prefetch_views"].append(ev[0].elapsed_time(ev[1]))
+        t["ffn_views"].append(ev[1].elapsed_time(ev[2]))
+        t["prefetch_split"].append(ev[3].elapsed_time(ev[4]))
+        t["ffn_split"].append(ev[4].elapsed_time(ev[5]))
+    m = {k: float(np.mean(v)) for k, v in t.items()}
+    phys = sbs[0].physical_bytes
+    gran = sbs[0].granularity
+    del views
+    for sb in sbs:
+        sb.destroy()
+    return {"ffn_ms_views": round(m["ffn_views"], 3), "ffn_ms_split": round(m["ffn_split"], 3),
+            "ffn_views_over_split": round(m["ffn_views"] / m["ffn_split"], 4),
+            "prefetch_us_views": round(m["prefetch_views"] * 1e3, 1),
+            "prefetch_us_split": round(m["prefetch_split"] * 1e3, 1),
+            "physical_bytes_per_projection": phys, "vmm_granularity": gran,
+            "steps": steps,
+            "note": "per-rank [E+B] views on hipMemMap'd chunks vs separate home/pool tensors"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +335,10 @@ def main():
     ap.add_argument("--overlap", action="store_true",
                     help="also time two pipelined micro-batches with dispatch/combine on a "
                          "second stream at a 32-CU budget against running them back to back")
+    ap.add_argument("--views", action="store_true",
+                    help="also time prefetch and the FFN over per-rank [E+B] views on virtual "
+                         "memory (SymmetricBuffer) beside ordinary home/pool tensors; needs "
+                         "~45 GB more HBM at the headline shape")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before warmup, run torch.neg over a float32 buffer of MIB MiB "
                          "three times: a plain kernel of known traffic (reads and writes "
@@ -474,6 +532,9 @@ def main():
         "combine_us_copy_mode": round((t_comb + t_copy) * 1e6, 1),
         "note": f"one copy of the used slots (real + padding rows) per call, timed at maxvio {t_last}"}
     del scratch
+
+    if args.views:
+        result["views"] = time_views(w, buf, batches, home, pool, x, max(2, args.steps // 2))
 
     if args.overlap:
         result["overlap"] = time_overlap(w, batches, home, pool, max(2, args.steps // 2),

@@ -12,6 +12,11 @@ device memory and the current stream; nothing is computed in Python.
     buf.expert_ffn(plan, x_nvs, home, pool, z, y)   # moonep_expert_ffn
                                                     # (= expert_gateup + expert_down)
     out, rw_sk = buf.combine(plan, y, rw_nvs)       # moonep_combine
+
+`SymmetricBuffer` is the README's [E+B,H,H'] weight (or fp32 gradient) buffer
+of one projection on virtual memory (moonep_symbuf_*): per-rank views whose
+rows [0,E) map every rank's home chunk, with the *_views methods addressing
+experts purely by row index.
 """
 from __future__ import annotations
 
@@ -22,7 +27,7 @@ import torch
 from . import _abi
 from ._abi import MoonepError, lib  # noqa: F401
 
-__all__ = ["Buffer", "Plan", "MoonepError", "lib"]
+__all__ = ["Buffer", "Plan", "SymmetricBuffer", "MoonepError", "lib", "vmm_granularity"]
 
 
 def _stream():
@@ -203,6 +208,35 @@ class Buffer:
                    "moonep_expert_ffn")
         return z_ws, y_nvs
 
+    def _views(self, views):
+        R, E, B, H, Hp = self.R, self.E, self.B, self.H, self.Hp
+        if len(views) != 3:
+            raise ValueError("three projections (gate, up, down) expected")
+        for i, t in enumerate(views):
+            _dev_ptr(t, torch.bfloat16, (R, E + B, H, Hp), f"views[{i}]")
+        return _abi.ptr3(views)
+
+    def prefetch_weight_views(self, plan, views):
+        """prefetch_weight over per-rank [E+B] views (views[p] [R,E+B,H,Hp])."""
+        _abi.check(lib().moonep_prefetch_weight_views(self._h, ctypes.byref(plan.struct),
+                                                      self._views(views), _stream()),
+                   "moonep_prefetch_weight_views")
+
+    def expert_ffn_views(self, plan, x_nvs, views, z_ws=None, y_nvs=None, rank=-1):
+        """expert_ffn with experts located by row index in rank d's [E+B] view."""
+        R, NvS, H, Hp = self.R, self.NvS, self.H, self.Hp
+        if z_ws is None:
+            z_ws = torch.empty((R, NvS, Hp), dtype=torch.bfloat16, device=x_nvs.device)
+        if y_nvs is None:
+            y_nvs = torch.empty((R, NvS, H), dtype=torch.bfloat16, device=x_nvs.device)
+        args = (int(rank), _dev_ptr(x_nvs, torch.bfloat16, (R, NvS, H), "x_nvs"),
+                self._views(views),
+                _dev_ptr(z_ws, torch.bfloat16, (R, NvS, Hp), "z_ws"),
+                _dev_ptr(y_nvs, torch.bfloat16, (R, NvS, H), "y_nvs"))
+        _abi.check(lib().moonep_expert_ffn_views(self._h, ctypes.byref(plan.struct), *args,
+                                                 _stream()), "moonep_expert_ffn_views")
+        return z_ws, y_nvs
+
     def expert_gateup(self, plan, x_nvs, home, pool, z_nvs=None, rank=-1):
         R, NvS, H, Hp = self.R, self.NvS, self.H, self.Hp
         if z_nvs is None:
@@ -247,6 +281,27 @@ class Buffer:
                                                _stream()), "moonep_expert_ffn_bwd")
         return dz_ws, dg_nvs, du_nvs, dx_nvs
 
+    def expert_ffn_bwd_views(self, plan, x_nvs, dy_nvs, views, dz_ws=None, dg_nvs=None,
+                             du_nvs=None, dx_nvs=None, rank=-1):
+        """expert_ffn_bwd with experts located by row index in rank d's [E+B] view."""
+        R, NvS, H, Hp = self.R, self.NvS, self.H, self.Hp
+        dev = x_nvs.device
+        new = lambda W: torch.empty((R, NvS, W), dtype=torch.bfloat16, device=dev)
+        dz_ws = new(Hp) if dz_ws is None else dz_ws
+        dg_nvs = new(Hp) if dg_nvs is None else dg_nvs
+        du_nvs = new(Hp) if du_nvs is None else du_nvs
+        dx_nvs = new(H) if dx_nvs is None else dx_nvs
+        args = (int(rank), _dev_ptr(x_nvs, torch.bfloat16, (R, NvS, H), "x_nvs"),
+                _dev_ptr(dy_nvs, torch.bfloat16, (R, NvS, H), "dy_nvs"),
+                self._views(views),
+                _dev_ptr(dz_ws, torch.bfloat16, (R, NvS, Hp), "dz_ws"),
+                _dev_ptr(dg_nvs, torch.bfloat16, (R, NvS, Hp), "dg_nvs"),
+                _dev_ptr(du_nvs, torch.bfloat16, (R, NvS, Hp), "du_nvs"),
+                _dev_ptr(dx_nvs, torch.bfloat16, (R, NvS, H), "dx_nvs"))
+        _abi.check(lib().moonep_expert_ffn_bwd_views(self._h, ctypes.byref(plan.struct), *args,
+                                                     _stream()), "moonep_expert_ffn_bwd_views")
+        return dz_ws, dg_nvs, du_nvs, dx_nvs
+
     def expert_wgrad(self, plan, a_nvs, b_nvs, grad_home, reduce_buf, rank=-1):
         R, NvS, E, B, H, Hp = self.R, self.NvS, self.E, self.B, self.H, self.Hp
         args = (int(rank), _dev_ptr(a_nvs, torch.bfloat16, (R, NvS, H), "a_nvs"),
@@ -273,6 +328,60 @@ class Buffer:
                                            out.ctypes.data_as(ctypes.c_void_p), _stream()),
                    "moonep_read_stats")
         return out
+
+
+def vmm_granularity():
+    """Minimum virtual-memory allocation granularity of the current device, bytes."""
+    g = ctypes.c_int64()
+    _abi.check(lib().moonep_vmm_granularity(ctypes.byref(g)), "moonep_vmm_granularity")
+    return int(g.value)
+
+
+class SymmetricBuffer:
+    """One projection's [E+B,H,H'] buffer for the R ranks of `buf`, built on
+    virtual memory by the library (moonep_symbuf_create): bf16 weights (README
+    "Weight buffer") or fp32 gradients ("Gradient buffer").
+
+    views [R,E+B,H,Hp]: rank d's contiguous [E+B] range; rows [0,E) map the R
+                        home chunks, rows [E,E+B) rank d's own slot chunk
+    home  [E,H,Hp]:     the home chunks (home[p] / grad_home of the other calls)
+    slots [R,B,H,Hp]:   the slot chunks (pool[p] / the [R,B] reduce view)
+
+    The three tensors alias the same physical memory.  They do not own it:
+    drop them before destroy()."""
+
+    def __init__(self, buf, dtype=torch.bfloat16):
+        elem = {torch.bfloat16: 2, torch.float32: 4}.get(dtype)
+        if elem is None:
+            raise TypeError("SymmetricBuffer holds bf16 weights or fp32 gradients")
+        self._b = ctypes.c_void_p()
+        dev = buf.device if buf.device.index is not None else \
+            torch.device("cuda", torch.cuda.current_device())
+        with torch.cuda.device(dev):
+            _abi.check(lib().moonep_symbuf_create(buf._h, elem, ctypes.byref(self._b)),
+                       "moonep_symbuf_create")
+        info = _abi.MoonepSymbufInfo()
+        _abi.check(lib().moonep_symbuf_info(self._b, ctypes.byref(info)), "moonep_symbuf_info")
+        self.row_bytes = int(info.row_bytes)
+        self.physical_bytes = int(info.physical_bytes)
+        self.granularity = int(info.granularity)
+        R, E, B, H, Hp = buf.R, buf.E, buf.B, buf.H, buf.Hp
+        self.views = _abi.device_tensor(info.views, (R, E + B, H, Hp), dtype, dev.index)
+        self.home = _abi.device_tensor(info.home, (E, H, Hp), dtype, dev.index)
+        self.slots = (_abi.device_tensor(info.slots, (R, B, H, Hp), dtype, dev.index) if B
+                      else torch.empty((R, 0, H, Hp), dtype=dtype, device=dev))
+
+    def destroy(self):
+        if self._b:
+            self.views = self.home = self.slots = None
+            _abi.check(lib().moonep_symbuf_destroy(self._b), "moonep_symbuf_destroy")
+            self._b = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
 
 
 # fail at import time, loudly, when the native library is missing

@@ -28,6 +28,12 @@ class MoonepPlan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in PLAN_ARRAYS]
 
 
+class MoonepSymbufInfo(ctypes.Structure):
+    _fields_ = [("views", ctypes.c_void_p), ("home", ctypes.c_void_p), ("slots", ctypes.c_void_p),
+                ("row_bytes", ctypes.c_int64), ("physical_bytes", ctypes.c_int64),
+                ("granularity", ctypes.c_int64)]
+
+
 class MoonepError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
@@ -72,6 +78,15 @@ def lib():
         "moonep_expert_wgrad": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, vp, vp, vp, vp]),
         "moonep_reduce_grad": (i32, [vp, ctypes.POINTER(MoonepPlan), P3, P3, vp]),
         "moonep_read_stats": (i32, [vp, ctypes.POINTER(MoonepPlan), vp, vp]),
+        "moonep_vmm_granularity": (i32, [ctypes.POINTER(i64)]),
+        "moonep_symbuf_create": (i32, [vp, i32, ctypes.POINTER(vp)]),
+        "moonep_symbuf_info": (i32, [vp, ctypes.POINTER(MoonepSymbufInfo)]),
+        "moonep_symbuf_destroy": (i32, [vp]),
+        "moonep_prefetch_weight_views": (i32, [vp, ctypes.POINTER(MoonepPlan), P3, vp]),
+        "moonep_expert_ffn_views": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, P3, vp, vp,
+                                          vp]),
+        "moonep_expert_ffn_bwd_views": (i32, [vp, ctypes.POINTER(MoonepPlan), i32, vp, vp, P3,
+                                              vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -106,3 +121,63 @@ def plan_len(cfg: MoonepConfig, which: int) -> int:
 
 def ptr3(ts):
     return (ctypes.c_void_p * 3)(*[None if t is None else t.data_ptr() for t in ts])
+
+
+# -- device memory the library owns, seen as torch tensors (DLPack) ----------
+# DLPack's C structures (dlpack.h, version 0.x "DLManagedTensor"), declared
+# here because the capsule is built with ctypes.
+
+class _DLDevice(ctypes.Structure):
+    _fields_ = [("device_type", ctypes.c_int32), ("device_id", ctypes.c_int32)]
+
+
+class _DLDataType(ctypes.Structure):
+    _fields_ = [("code", ctypes.c_uint8), ("bits", ctypes.c_uint8), ("lanes", ctypes.c_uint16)]
+
+
+class _DLTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("device", _DLDevice), ("ndim", ctypes.c_int32),
+                ("dtype", _DLDataType), ("shape", ctypes.POINTER(ctypes.c_int64)),
+                ("strides", ctypes.POINTER(ctypes.c_int64)), ("byte_offset", ctypes.c_uint64)]
+
+
+class _DLManagedTensor(ctypes.Structure):
+    _fields_ = [("dl_tensor", _DLTensor), ("manager_ctx", ctypes.c_void_p),
+                ("deleter", ctypes.c_void_p)]
+
+
+_DL_ROCM = 10
+_DL_FLOAT, _DL_BFLOAT = 2, 4
+# The consumer reads the managed tensor again when its tensor dies (to find the
+# deleter, which is NULL here), so the structures stay alive for the process.
+_dl_keep = []
+
+
+def device_tensor(ptr, shape, dtype, device_index):
+    """Torch tensor over `ptr` (device memory owned by the library, not by
+    torch): dense row-major `shape` of bf16 or fp32.  The tensor does not
+    keep the memory alive; its owner must outlive every use of it."""
+    return wrap_memory(ptr, shape, dtype, _DL_ROCM, device_index)
+
+
+def wrap_memory(ptr, shape, dtype, device_type, device_index):
+    """DLPack import of foreign memory (device_type 10 = ROCm, 1 = CPU)."""
+    import torch
+    code, bits = {torch.bfloat16: (_DL_BFLOAT, 16), torch.float32: (_DL_FLOAT, 32)}[dtype]
+    shp = (ctypes.c_int64 * len(shape))(*shape)
+    mt = _DLManagedTensor()
+    mt.dl_tensor.data = ptr
+    mt.dl_tensor.device = _DLDevice(device_type, device_index)
+    mt.dl_tensor.ndim = len(shape)
+    mt.dl_tensor.dtype = _DLDataType(code, bits, 1)
+    mt.dl_tensor.shape = shp
+    mt.dl_tensor.strides = None
+    mt.dl_tensor.byte_offset = 0
+    mt.manager_ctx = None
+    mt.deleter = None
+    _dl_keep.append((mt, shp))
+    new_capsule = ctypes.pythonapi.PyCapsule_New
+    new_capsule.restype = ctypes.py_object
+    new_capsule.argtypes = [ctypes.c_void_p, ctypes.c_char_p, ctypes.c_void_p]
+    cap = new_capsule(ctypes.addressof(mt), b"dltensor", None)
+    return torch.utils.dlpack.from_dlpack(cap)

@@ -57,10 +57,6 @@ bool dims_from_config(const moonep_config_t* cfg, Dims* out) {
 
 using namespace moonep;
 
-struct moonep_ctx {
-  Ctx c;
-};
-
 static bool aligned(const void* p, size_t a) {
   return ((uintptr_t)p % a) == 0;
 }
@@ -69,12 +65,62 @@ static moonep_status_t hip_status(hipError_t e) {
   return e == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
 }
 
+// Separate tensors: home [E] shared by every rank, pool [R*B].
+static WeightRef split_ref(const Dims& d, const uint16_t* const home[3],
+                           const uint16_t* const pool[3]) {
+  WeightRef w;
+  for (int p = 0; p < 3; ++p) {
+    w.home[p] = home[p];
+    w.pool[p] = const_cast<uint16_t*>(pool[p]);
+  }
+  w.home_stride = 0;
+  w.pool_stride = d.B;
+  return w;
+}
+
+// Per-rank [E+B] views, back to back: rank d's row i at views + (d*(E+B)+i) rows.
+static WeightRef views_ref(const Dims& d, const uint16_t* const views[3]) {
+  WeightRef w;
+  const int64_t rs = (int64_t)d.H * d.Hp;
+  for (int p = 0; p < 3; ++p) {
+    w.home[p] = views[p];
+    w.pool[p] = (views[p] && d.B > 0) ? const_cast<uint16_t*>(views[p]) + d.E * rs : nullptr;
+  }
+  w.home_stride = d.E + d.B;
+  w.pool_stride = d.E + d.B;
+  return w;
+}
+
 static bool plan_ok(const moonep_plan_t* p) {
   if (!p) return false;
   const int32_t* a[] = {p->counts, p->dest, p->src, p->cu_seqlens,
                         p->seg_tokens, p->prefetch_src, p->stats, p->aux};
   for (const int32_t* q : a)
     if (!q || !aligned(q, 4)) return false;
+  return true;
+}
+
+static hipError_t run_ffn(const Ctx& c, const moonep_plan_t& p, int rank, const uint16_t* x,
+                          const WeightRef& w, uint16_t* z, uint16_t* y, hipStream_t s) {
+  hipError_t e = launch_gateup(c, p, rank, x, w, z, s);
+  if (e == hipSuccess) e = launch_down(c, p, rank, z, w, y, s);
+  return e;
+}
+
+// Buffers of the FFN backward: all present and 16-byte aligned; dZ, dG and dU
+// distinct from each other and from every other buffer; dX may reuse the
+// storage of dY or X (both are consumed before dX is written).
+static bool bwd_buffers_ok(const Ctx& c, int rank, const void* x, const void* dy,
+                           const void* dz, const void* dg, const void* du, const void* dx) {
+  if (rank < -1 || rank >= c.d.R) return false;
+  const void* all[] = {x, dy, dz, dg, du, dx};
+  for (const void* q : all)
+    if (!q || !aligned(q, 16)) return false;
+  const void* ws[] = {dz, dg, du};
+  const void* other[] = {x, dy, dx, dz, dg, du};
+  for (int i = 0; i < 3; ++i)
+    for (int k = 0; k < 6; ++k)
+      if (ws[i] == other[k] && k != 3 + i) return false;
   return true;
 }
 
@@ -213,7 +259,7 @@ moonep_status_t moonep_prefetch_weight(moonep_handle_t h, const moonep_plan_t* p
     if (h->c.d.B > 0 && (!pool[p] || !aligned(pool[p], 16))) return MOONEP_ERR_ARG;
   }
   if (h->c.d.B == 0) return MOONEP_OK;
-  return hip_status(launch_prefetch(h->c, *plan, home, pool, stream));
+  return hip_status(launch_prefetch(h->c, *plan, split_ref(h->c.d, home, pool), stream));
 }
 
 static bool weights_ok(const Ctx& c, const uint16_t* const home[3],
@@ -223,6 +269,13 @@ static bool weights_ok(const Ctx& c, const uint16_t* const home[3],
     if (!home[p] || !aligned(home[p], 16)) return false;
     if (c.d.B > 0 && (!pool[p] || !aligned(pool[p], 16))) return false;
   }
+  return true;
+}
+
+static bool views_ok(const uint16_t* const views[3], int p0, int p1) {
+  if (!views) return false;
+  for (int p = p0; p < p1; ++p)
+    if (!views[p] || !aligned(views[p], 16)) return false;
   return true;
 }
 
@@ -236,7 +289,8 @@ moonep_status_t moonep_expert_gateup(moonep_handle_t h, const moonep_plan_t* pla
   if (!aligned(x_nvs, 16) || !aligned(z_nvs, 16) || (void*)z_nvs == (void*)x_nvs)
     return MOONEP_ERR_ARG;
   if (!weights_ok(h->c, home, pool, 0, 2)) return MOONEP_ERR_ARG;
-  return hip_status(launch_gateup(h->c, *plan, rank, x_nvs, home, pool, z_nvs, stream));
+  return hip_status(launch_gateup(h->c, *plan, rank, x_nvs, split_ref(h->c.d, home, pool), z_nvs,
+                                  stream));
 }
 
 moonep_status_t moonep_expert_down(moonep_handle_t h, const moonep_plan_t* plan,
@@ -249,7 +303,8 @@ moonep_status_t moonep_expert_down(moonep_handle_t h, const moonep_plan_t* plan,
   if (!aligned(z_nvs, 16) || !aligned(y_nvs, 16) || (void*)z_nvs == (void*)y_nvs)
     return MOONEP_ERR_ARG;
   if (!weights_ok(h->c, home, pool, 2, 3)) return MOONEP_ERR_ARG;
-  return hip_status(launch_down(h->c, *plan, rank, z_nvs, home, pool, y_nvs, stream));
+  return hip_status(launch_down(h->c, *plan, rank, z_nvs, split_ref(h->c.d, home, pool), y_nvs,
+                                stream));
 }
 
 moonep_status_t moonep_expert_ffn(moonep_handle_t h, const moonep_plan_t* plan,
@@ -262,9 +317,30 @@ moonep_status_t moonep_expert_ffn(moonep_handle_t h, const moonep_plan_t* plan,
   if (!aligned(x_nvs, 16) || !aligned(z_ws, 16) || !aligned(y_nvs, 16)) return MOONEP_ERR_ARG;
   if ((void*)z_ws == (void*)x_nvs || (void*)z_ws == (void*)y_nvs) return MOONEP_ERR_ARG;
   if (!weights_ok(h->c, home, pool, 0, 3)) return MOONEP_ERR_ARG;
-  hipError_t e = launch_gateup(h->c, *plan, rank, x_nvs, home, pool, z_ws, stream);
-  if (e == hipSuccess) e = launch_down(h->c, *plan, rank, z_ws, home, pool, y_nvs, stream);
-  return hip_status(e);
+  return hip_status(run_ffn(h->c, *plan, rank, x_nvs, split_ref(h->c.d, home, pool), z_ws, y_nvs,
+                            stream));
+}
+
+moonep_status_t moonep_expert_ffn_views(moonep_handle_t h, const moonep_plan_t* plan,
+                                        int32_t rank, const uint16_t* x_nvs,
+                                        const uint16_t* const views[3], uint16_t* z_ws,
+                                        uint16_t* y_nvs, hipStream_t stream) {
+  if (!h || !plan_ok(plan) || !x_nvs || !z_ws || !y_nvs) return MOONEP_ERR_ARG;
+  if (rank < -1 || rank >= h->c.d.R) return MOONEP_ERR_ARG;
+  if (!aligned(x_nvs, 16) || !aligned(z_ws, 16) || !aligned(y_nvs, 16)) return MOONEP_ERR_ARG;
+  if ((void*)z_ws == (void*)x_nvs || (void*)z_ws == (void*)y_nvs) return MOONEP_ERR_ARG;
+  if (!views_ok(views, 0, 3)) return MOONEP_ERR_ARG;
+  return hip_status(run_ffn(h->c, *plan, rank, x_nvs, views_ref(h->c.d, views), z_ws, y_nvs,
+                            stream));
+}
+
+moonep_status_t moonep_prefetch_weight_views(moonep_handle_t h, const moonep_plan_t* plan,
+                                             uint16_t* const views[3], hipStream_t stream) {
+  if (!h || !plan_ok(plan) || !views) return MOONEP_ERR_ARG;
+  const uint16_t* cv[3] = {views[0], views[1], views[2]};
+  if (!views_ok(cv, 0, 3)) return MOONEP_ERR_ARG;
+  if (h->c.d.B == 0) return MOONEP_OK;
+  return hip_status(launch_prefetch(h->c, *plan, views_ref(h->c.d, cv), stream));
 }
 
 moonep_status_t moonep_expert_ffn_bwd(moonep_handle_t h, const moonep_plan_t* plan,
@@ -273,22 +349,26 @@ moonep_status_t moonep_expert_ffn_bwd(moonep_handle_t h, const moonep_plan_t* pl
                                       const uint16_t* const pool[3], uint16_t* dz_ws,
                                       uint16_t* dg_nvs, uint16_t* du_nvs, uint16_t* dx_nvs,
                                       hipStream_t stream) {
-  if (!h || !plan_ok(plan) || !x_nvs || !dy_nvs || !dz_ws || !dg_nvs || !du_nvs || !dx_nvs)
+  if (!h || !plan_ok(plan)) return MOONEP_ERR_ARG;
+  if (!bwd_buffers_ok(h->c, rank, x_nvs, dy_nvs, dz_ws, dg_nvs, du_nvs, dx_nvs))
     return MOONEP_ERR_ARG;
-  if (rank < -1 || rank >= h->c.d.R) return MOONEP_ERR_ARG;
-  const void* all[] = {x_nvs, dy_nvs, dz_ws, dg_nvs, du_nvs, dx_nvs};
-  for (const void* q : all)
-    if (!aligned(q, 16)) return MOONEP_ERR_ARG;
-  // dZ, dG and dU are distinct from each other and from every other buffer;
-  // dX may reuse the storage of dY or X (both are consumed before dX is written)
-  const void* ws[] = {dz_ws, dg_nvs, du_nvs};
-  const void* other[] = {x_nvs, dy_nvs, dx_nvs, dz_ws, dg_nvs, du_nvs};
-  for (int i = 0; i < 3; ++i)
-    for (int k = 0; k < 6; ++k)
-      if (ws[i] == other[k] && k != 3 + i) return MOONEP_ERR_ARG;
   if (!weights_ok(h->c, home, pool, 0, 3)) return MOONEP_ERR_ARG;
-  return hip_status(launch_ffn_bwd(h->c, *plan, rank, x_nvs, dy_nvs, home, pool, dz_ws, dg_nvs,
-                                   du_nvs, dx_nvs, stream));
+  return hip_status(launch_ffn_bwd(h->c, *plan, rank, x_nvs, dy_nvs, split_ref(h->c.d, home, pool),
+                                   dz_ws, dg_nvs, du_nvs, dx_nvs, stream));
+}
+
+moonep_status_t moonep_expert_ffn_bwd_views(moonep_handle_t h, const moonep_plan_t* plan,
+                                            int32_t rank, const uint16_t* x_nvs,
+                                            const uint16_t* dy_nvs,
+                                            const uint16_t* const views[3], uint16_t* dz_ws,
+                                            uint16_t* dg_nvs, uint16_t* du_nvs,
+                                            uint16_t* dx_nvs, hipStream_t stream) {
+  if (!h || !plan_ok(plan)) return MOONEP_ERR_ARG;
+  if (!bwd_buffers_ok(h->c, rank, x_nvs, dy_nvs, dz_ws, dg_nvs, du_nvs, dx_nvs))
+    return MOONEP_ERR_ARG;
+  if (!views_ok(views, 0, 3)) return MOONEP_ERR_ARG;
+  return hip_status(launch_ffn_bwd(h->c, *plan, rank, x_nvs, dy_nvs, views_ref(h->c.d, views),
+                                   dz_ws, dg_nvs, du_nvs, dx_nvs, stream));
 }
 
 moonep_status_t moonep_expert_wgrad(moonep_handle_t h, const moonep_plan_t* plan,

@@ -157,9 +157,8 @@ hipError_t launch_gemm_schedule(const Ctx& c, const moonep_plan_t& p, hipStream_
 }
 
 hipError_t launch_gateup(const Ctx& c, const moonep_plan_t& p, int rank, const uint16_t* x_nvs,
-                         const uint16_t* const home[3], const uint16_t* const pool[3],
-                         uint16_t* z, hipStream_t s) {
-  FfnArgs a = ffn_args(c, p, rank, home, pool);
+                         const WeightRef& w, uint16_t* z, hipStream_t s) {
+  FfnArgs a = ffn_args(c, p, rank, w);
   a.x = x_nvs;
   a.z = z;
   a.ntn = (c.d.Hp + 127) / 128;
@@ -168,9 +167,8 @@ hipError_t launch_gateup(const Ctx& c, const moonep_plan_t& p, int rank, const u
 }
 
 hipError_t launch_down(const Ctx& c, const moonep_plan_t& p, int rank, const uint16_t* z,
-                       const uint16_t* const home[3], const uint16_t* const pool[3],
-                       uint16_t* y, hipStream_t s) {
-  FfnArgs a = ffn_args(c, p, rank, home, pool);
+                       const WeightRef& w, uint16_t* y, hipStream_t s) {
+  FfnArgs a = ffn_args(c, p, rank, w);
   a.zin = z;
   a.y = y;
   a.ntn = (c.d.H + BN - 1) / BN;

@@ -228,10 +228,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 }  // namespace
 
 hipError_t launch_ffn_bwd(const Ctx& c, const moonep_plan_t& p, int rank, const uint16_t* x,
-                          const uint16_t* dy, const uint16_t* const home[3],
-                          const uint16_t* const pool[3], uint16_t* dz, uint16_t* dg,
+                          const uint16_t* dy, const WeightRef& w, uint16_t* dz, uint16_t* dg,
                           uint16_t* du, uint16_t* dx, hipStream_t s) {
-  FfnArgs a = ffn_args(c, p, rank, home, pool);
+  FfnArgs a = ffn_args(c, p, rank, w);
   a.x = x; a.dy = dy; a.dz = dz; a.dg = dg; a.du = du; a.dx = dx;
   const int64_t slots = (int64_t)a.nranks * a.max_tiles;
   a.ntn = (c.d.Hp + BN - 1) / BN;

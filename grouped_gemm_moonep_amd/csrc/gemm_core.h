@@ -467,8 +467,9 @@ struct Tile {
 
 struct FfnArgs {
   const uint16_t* x;        // [R*NvS][H] (gate/up input)
-  const uint16_t* home[3];  // [E][H][Hp]
-  const uint16_t* pool[3];  // [R*B][H][Hp]
+  const uint16_t* home[3];  // rows [0,E) of rank d at home + d*hstride rows
+  const uint16_t* pool[3];  // rows [E,E+B) of rank d at pool + d*pstride rows
+  int64_t hstride, pstride;
   uint16_t* z;              // [R*NvS][Hp] (gate/up output)
   const uint16_t* zin;      // [R*NvS][Hp] (down input)
   uint16_t* y;              // [R*NvS][H]
@@ -485,7 +486,8 @@ struct FfnArgs {
 
 __device__ __forceinline__ const uint16_t* weight_row(const FfnArgs& a, int p, int d, int row) {
   const int64_t rs = (int64_t)a.H * a.Hp;
-  return row < a.E ? a.home[p] + (int64_t)row * rs : a.pool[p] + ((int64_t)d * a.B + row - a.E) * rs;
+  return row < a.E ? a.home[p] + ((int64_t)d * a.hstride + row) * rs
+                   : a.pool[p] + ((int64_t)d * a.pstride + row - a.E) * rs;
 }
 
 // Within a rank, tiles are taken in groups of up to kGroupM M-tiles of one
@@ -538,13 +540,15 @@ int64_t pad_grid(int64_t n) { return (n + kXcds - 1) / kXcds * kXcds; }
 }  // namespace
 
 static inline FfnArgs ffn_args(const Ctx& c, const moonep_plan_t& p, int rank,
-                        const uint16_t* const home[3], const uint16_t* const pool[3]) {
+                               const WeightRef& w) {
   const Dims& d = c.d;
   FfnArgs a;
   for (int i = 0; i < 3; ++i) {
-    a.home[i] = home[i];
-    a.pool[i] = pool[i];
+    a.home[i] = w.home[i];
+    a.pool[i] = w.pool[i];
   }
+  a.hstride = w.home_stride;
+  a.pstride = w.pool_stride;
   a.x = nullptr; a.z = nullptr; a.zin = nullptr; a.y = nullptr;
   a.dy = nullptr; a.dz = nullptr; a.dg = nullptr; a.du = nullptr; a.dx = nullptr;
   a.tiles = p.aux + d.aux.tiles; a.ntiles = p.aux + d.aux.ntiles;

@@ -55,6 +55,18 @@ struct Ctx {
 
 bool dims_from_config(const moonep_config_t* cfg, Dims* out);
 
+// Where the weight row `row` of rank d lives (projection p, H*Hp elements per
+// row): rows [0,E) at home[p] + (d*home_stride + row) rows, rows [E,E+B) at
+// pool[p] + (d*pool_stride + row-E) rows.  Separate tensors home [E] and
+// pool [R*B] have strides 0 and B; per-rank [E+B] views laid out back to back
+// ([R][E+B]) have home = the views, pool = the views + E rows, both strides
+// E+B.
+struct WeightRef {
+  const uint16_t* home[3];
+  uint16_t* pool[3];
+  int64_t home_stride, pool_stride;
+};
+
 // Kernel launchers (each returns hipGetLastError() after its launches).
 hipError_t launch_plan(const Ctx& c, const int32_t* topk, const int32_t* tpe,
                        const moonep_plan_t& p, hipStream_t s);
@@ -67,22 +79,19 @@ hipError_t launch_combine(const Ctx& c, const moonep_plan_t& p,
 hipError_t launch_copy_rows(const Ctx& c, const moonep_plan_t& p,
                             const uint16_t* src, int W, uint16_t* dst,
                             hipStream_t s);
-hipError_t launch_prefetch(const Ctx& c, const moonep_plan_t& p,
-                           const uint16_t* const home[3],
-                           uint16_t* const pool[3], hipStream_t s);
+hipError_t launch_prefetch(const Ctx& c, const moonep_plan_t& p, const WeightRef& w,
+                           hipStream_t s);
 hipError_t launch_reduce_grad(const Ctx& c, const moonep_plan_t& p,
                               float* const gh[3], float* const rb[3],
                               hipStream_t s);
 hipError_t launch_gemm_schedule(const Ctx& c, const moonep_plan_t& p, hipStream_t s);
 hipError_t launch_gateup(const Ctx& c, const moonep_plan_t& p, int rank,
-                         const uint16_t* x_nvs, const uint16_t* const home[3],
-                         const uint16_t* const pool[3], uint16_t* z, hipStream_t s);
+                         const uint16_t* x_nvs, const WeightRef& w, uint16_t* z,
+                         hipStream_t s);
 hipError_t launch_down(const Ctx& c, const moonep_plan_t& p, int rank,
-                       const uint16_t* z, const uint16_t* const home[3],
-                       const uint16_t* const pool[3], uint16_t* y, hipStream_t s);
+                       const uint16_t* z, const WeightRef& w, uint16_t* y, hipStream_t s);
 hipError_t launch_ffn_bwd(const Ctx& c, const moonep_plan_t& p, int rank,
-                          const uint16_t* x, const uint16_t* dy,
-                          const uint16_t* const home[3], const uint16_t* const pool[3],
+                          const uint16_t* x, const uint16_t* dy, const WeightRef& w,
                           uint16_t* dz, uint16_t* dg, uint16_t* du, uint16_t* dx,
                           hipStream_t s);
 hipError_t launch_wgrad(const Ctx& c, const moonep_plan_t& p, int rank,
@@ -94,3 +103,8 @@ constexpr int kGemmTileM = 256;
 constexpr int kWgradTileM = 64;   // tokens per k-step of the weight gradient
 
 }  // namespace moonep
+
+// The object behind a moonep_handle_t.
+struct moonep_ctx {
+  moonep::Ctx c;
+};

@@ -162,12 +162,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 
 // prefetch: work item = (used slot, projection, chunk of a row).
 struct PrefetchArgs {
-  const u32x4* home[3];  // [E][row_vecs]
-  u32x4* pool[3];        // [R*B][row_vecs]
+  const u32x4* home[3];  // home row e of rank d at home + (d*hstride + e) rows
+  u32x4* pool[3];        // slot j of rank d at pool + (d*pstride + j) rows
   const int32_t* pf;     // [R*B] prefetch_src
   const int32_t* aux_pf; // used slot list
   const int32_t* aux_pf_n;
   int64_t row_vecs;
+  int64_t hstride, pstride;
+  int B;
   int chunk_vecs, nchunks;
 };
 
@@ -180,8 +182,9 @@ __global__ __launch_bounds__(kThreads) void prefetch_kernel(PrefetchArgs a) {
     const int q = (int)(it / ((int64_t)a.nchunks * 3));
     const int slot = a.aux_pf[q];
     const int e = a.pf[slot];
-    const u32x4* src = a.home[proj] + (int64_t)e * a.row_vecs;
-    u32x4* dst = a.pool[proj] + (int64_t)slot * a.row_vecs;
+    const int d = slot / a.B;
+    const u32x4* src = a.home[proj] + ((int64_t)d * a.hstride + e) * a.row_vecs;
+    u32x4* dst = a.pool[proj] + ((int64_t)d * a.pstride + slot - d * a.B) * a.row_vecs;
     const int64_t v0 = (int64_t)chunk * a.chunk_vecs;
     int64_t v1 = v0 + a.chunk_vecs;
     if (v1 > a.row_vecs) v1 = a.row_vecs;
@@ -325,14 +328,17 @@ hipError_t launch_copy_rows(const Ctx& c, const moonep_plan_t& p, const uint16_t
   return hipGetLastError();
 }
 
-hipError_t launch_prefetch(const Ctx& c, const moonep_plan_t& p, const uint16_t* const home[3],
-                           uint16_t* const pool[3], hipStream_t s) {
+hipError_t launch_prefetch(const Ctx& c, const moonep_plan_t& p, const WeightRef& w,
+                           hipStream_t s) {
   const Dims& d = c.d;
   PrefetchArgs a;
   for (int i = 0; i < 3; ++i) {
-    a.home[i] = (const u32x4*)home[i];
-    a.pool[i] = (u32x4*)pool[i];
+    a.home[i] = (const u32x4*)w.home[i];
+    a.pool[i] = (u32x4*)w.pool[i];
   }
+  a.hstride = w.home_stride;
+  a.pstride = w.pool_stride;
+  a.B = d.B;
   a.pf = p.prefetch_src;
   a.aux_pf = p.aux + d.aux.pf;
   a.aux_pf_n = p.aux + d.aux.pf_n;

@@ -268,6 +268,92 @@ moonep_status_t moonep_reduce_grad(moonep_handle_t h,
                                    float* const reduce_buf[3],
                                    hipStream_t stream);
 
+/* ---- Symmetric [E+B,H,Hp] buffers on virtual memory ----
+ *
+ * The README's contract ("Usage > Integration > Weight buffer", "Gradient
+ * buffer") is one contiguous virtual range [E+B,H,Hp] per projection and
+ * rank.  Its rows [0,E) are every rank's home experts, each chunk physically
+ * the home rank's memory mapped everywhere; its rows [E,E+B) are the rank's
+ * prefetch slots (for fp32 gradients: its reduce buffer), from a separate
+ * allocation.  A symbuf builds exactly that for the R ranks of one GPU with
+ * hipMemCreate / hipMemAddressReserve / hipMemMap on the current device:
+ *   physical: per rank d, one chunk of E/R rows (home) and one of B rows
+ *             (slots), so E + R*B rows in all;
+ *   views [R,E+B,H,Hp]: rank d's [E+B] view starts at row d*(E+B); its rows
+ *             [0,E) map the R home chunks in rank order, its rows [E,E+B) its
+ *             own slot chunk;
+ *   home  [E,H,Hp]: the home chunks in rank order;
+ *   slots [R,B,H,Hp]: the slot chunks in rank order (for gradients: the
+ *             README's [R,B,H,Hp] view of every rank's reduce buffer).
+ * The ranges alias: a write through one is seen through every other range
+ * that maps the same chunk (in stream order).  `home` and `slots` are what
+ * the entry points above take as home[p]/pool[p] and grad_home/reduce_buf;
+ * `views` is what the *_views entry points below take.  Rows start
+ * uninitialised. */
+typedef struct moonep_symbuf* moonep_symbuf_t;
+
+typedef struct {
+  void* views;             /* device address, [R,E+B,H,Hp]                   */
+  void* home;              /* device address, [E,H,Hp]                       */
+  void* slots;             /* device address, [R,B,H,Hp]; NULL when B == 0   */
+  int64_t row_bytes;       /* H*Hp*elem_bytes                                */
+  int64_t physical_bytes;  /* (E + R*B) * row_bytes                          */
+  int64_t granularity;     /* the device's minimum VMM granularity, bytes    */
+} moonep_symbuf_info_t;
+
+/* Minimum VMM allocation granularity of the current device, bytes (host
+ * out). */
+moonep_status_t moonep_vmm_granularity(int64_t* out);
+
+/* Create the symbuf of one projection for the handle's configuration, on
+ * the current device.  elem_bytes: 2 for bf16 weights, 4 for fp32
+ * gradients.  (E/R)*H*Hp*elem_bytes and B*H*Hp*elem_bytes must be multiples
+ * of the granularity (MOONEP_ERR_CONFIG otherwise).  MOONEP_ERR_NOMEM when
+ * the physical memory is not there, MOONEP_ERR_HIP when another VMM call
+ * fails; on any error nothing stays allocated.  The symbuf does not depend
+ * on the handle after this call. */
+moonep_status_t moonep_symbuf_create(moonep_handle_t h, int32_t elem_bytes,
+                                     moonep_symbuf_t* out);
+
+/* Addresses and sizes of a symbuf (host out). */
+moonep_status_t moonep_symbuf_info(moonep_symbuf_t b, moonep_symbuf_info_t* out);
+
+/* Synchronise the symbuf's device, then unmap and free everything it holds.
+ * NULL is a no-op. */
+moonep_status_t moonep_symbuf_destroy(moonep_symbuf_t b);
+
+/* prefetch_weight over per-rank views, the README's own signature (rows
+ * [0,E) of each full_*_weight are the sources, rows [E,E+B) the slots):
+ * views[p] [R,E+B,H,Hp] bf16 (a symbuf's `views`, or any tensor of that
+ * layout), and for every used slot (d,j): row E+j of rank d's view becomes
+ * a bit copy of row prefetch_src[d][j] of the same view.  HOST array of 3
+ * device pointers. */
+moonep_status_t moonep_prefetch_weight_views(moonep_handle_t h,
+                                             const moonep_plan_t* plan,
+                                             uint16_t* const views[3],
+                                             hipStream_t stream);
+
+/* moonep_expert_ffn with every expert located purely by row index in rank
+ * d's [E+B] view (README "Usage > Integration": the grouped GEMM consumes one
+ * [E+B,H,H'] tensor per projection selected by cu_seqlens): row i of rank d
+ * is views[p] + (d*(E+B) + i)*H*Hp.  Otherwise identical to
+ * moonep_expert_ffn, including aliasing rules and results. */
+moonep_status_t moonep_expert_ffn_views(moonep_handle_t h, const moonep_plan_t* plan,
+                                        int32_t rank, const uint16_t* x_nvs,
+                                        const uint16_t* const views[3],
+                                        uint16_t* z_ws, uint16_t* y_nvs,
+                                        hipStream_t stream);
+
+/* moonep_expert_ffn_bwd with weights located as in moonep_expert_ffn_views. */
+moonep_status_t moonep_expert_ffn_bwd_views(moonep_handle_t h,
+                                            const moonep_plan_t* plan, int32_t rank,
+                                            const uint16_t* x_nvs,
+                                            const uint16_t* dy_nvs,
+                                            const uint16_t* const views[3],
+                                            uint16_t* dz_ws, uint16_t* dg_nvs,
+                                            uint16_t* du_nvs, uint16_t* dx_nvs,
+                                            hipStream_t stream);
+
 /* Synchronise `stream` and copy the plan's stats array to host_stats
  * (MOONEP_STAT_FIXED + 2R int32, HOST memory).  For tests and reports. */
 moonep_status_t moonep_read_stats(moonep_handle_t h, const moonep_plan_t* plan,

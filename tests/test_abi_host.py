@@ -98,3 +98,31 @@ def test_null_arguments_rejected_on_host():
                                    None) == ERR
     assert lib.moonep_reduce_grad(None, ctypes.byref(plan), P3(), P3(), None) == ERR
     assert lib.moonep_read_stats(None, ctypes.byref(plan), None, None) == ERR
+    assert lib.moonep_vmm_granularity(None) == ERR
+    out = ctypes.c_void_p()
+    assert lib.moonep_symbuf_create(None, 2, ctypes.byref(out)) == ERR
+    assert lib.moonep_symbuf_info(None, None) == ERR
+    assert lib.moonep_symbuf_destroy(None) == _abi.MOONEP_OK
+    assert lib.moonep_prefetch_weight_views(None, ctypes.byref(plan), P3(), None) == ERR
+    assert lib.moonep_expert_ffn_views(None, ctypes.byref(plan), -1, None, P3(), None, None,
+                                       None) == ERR
+    assert lib.moonep_expert_ffn_bwd_views(None, ctypes.byref(plan), -1, None, None, P3(), None,
+                                           None, None, None, None) == ERR
+
+
+def test_dlpack_wrapper_layout():
+    """The DLPack structures the binding builds by hand (to show library-owned
+    device memory as torch tensors) import correctly; checked on host memory
+    with device type CPU."""
+    import numpy as np
+    import torch
+    a = np.arange(2 * 3 * 4, dtype=np.float32).reshape(2, 3, 4)
+    t = _abi.wrap_memory(a.ctypes.data, (2, 3, 4), torch.float32, 1, 0)
+    assert t.shape == (2, 3, 4) and t.dtype == torch.float32 and t.is_contiguous()
+    assert t.data_ptr() == a.ctypes.data
+    assert torch.equal(t, torch.from_numpy(a))
+    t[1, 2, 3] = -5.0
+    assert a[1, 2, 3] == -5.0
+    src = torch.arange(16, dtype=torch.float32).to(torch.bfloat16)
+    b = _abi.wrap_memory(src.data_ptr(), (4, 4), torch.bfloat16, 1, 0)
+    assert b.dtype == torch.bfloat16 and torch.equal(b.reshape(-1), src)

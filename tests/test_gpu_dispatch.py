@@ -110,11 +110,13 @@ def test_copy_mode_equals_zero_copy(target):
     b = torch.full((w.R, buf.NvS, w.H), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
     b, rb = buf.dispatch(plan, x, dev(rw), x_nvs=b, zero_copy=False)
     ah, bh = host_bf16(a), host_bf16(b)
+    rah, rbh = ra.cpu().numpy().view(np.uint32), rb.cpu().numpy().view(np.uint32)
     for d in range(w.R):
         end = p.cu_seqlens[d, -1]
         assert np.array_equal(ah[d, :end], bh[d, :end])
         assert (bh[d, end:] == SENTINEL).all()
-    assert torch.equal(ra, rb)
+        # rw_nvs past the last segment is not written by either call
+        assert np.array_equal(rah[d, :end], rbh[d, :end])
     o1, g1 = buf.combine(plan, a, ra)
     o2, g2 = buf.combine(plan, b, rb, zero_copy=False)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(g1, g2)

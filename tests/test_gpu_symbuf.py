@@ -1,0 +1,236 @@
+"""Symmetric [E+B,H,H'] buffers on virtual memory (moonep_symbuf_*) on the
+GPU: the README's weight and gradient buffer layout ("Usage > Integration >
+Weight buffer", "Gradient buffer").
+
+* every rank's view maps the same physical home chunks (a write through any
+  range is read through every other range), and its rows [E,E+B) are its own
+  slots;
+* prefetch_weight_views fills rows [E,E+B) of each view from rows [0,E) of
+  the same view, as the oracle's plan says (prefetch_src), bit for bit;
+* the grouped FFN, forward and backward, over the views (experts located by
+  row index only) is bit-identical to the same call over the symbuf's
+  home/slots ranges and over ordinary device tensors, whose parity with the
+  oracle the FFN tests establish;
+* an fp32 gradient symbuf takes the weight gradients and reduce_grad through
+  its home and slots ranges, bit-identical to ordinary tensors, and its
+  per-rank views show the reduce slots."""
+import numpy as np
+import pytest
+import torch
+
+import moonep_synth as synth
+import oracle
+from gpu_util import buffer_for, dev, dev_bf16, log
+
+pytestmark = pytest.mark.gpu
+
+
+def bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def same(a, b):
+    return torch.equal(bits(a), bits(b))
+
+
+def symbufs(buf, w, n=3, dtype=torch.bfloat16):
+    from grouped_gemm_moonep_amd import SymmetricBuffer, vmm_granularity
+    g = vmm_granularity()
+    elem = 2 if dtype == torch.bfloat16 else 4
+    row = w.H * w.Hp * elem
+    if (w.E // w.R) * row % g or w.B * row % g:
+        pytest.skip(f"{w.name}: chunks of {row} B rows are not multiples of the "
+                    f"{g} B VMM granularity")
+    log(f"symbuf {w.name} {dtype} granularity={g}")
+    return [SymmetricBuffer(buf, dtype) for _ in range(n)]
+
+
+def filled_weights(buf, w):
+    sbs = symbufs(buf, w)
+    for i, sb in enumerate(sbs):
+        synth.expert_weights_device(w, i, sb.home)
+        bits(sb.slots).fill_(0x7F7F)
+    return sbs
+
+
+def test_views_alias_home_and_slots():
+    w = synth.WORKLOADS["mid_r8_s1024_k4_e32"]
+    R, E, B, H, Hp = w.R, w.E, w.B, w.H, w.Hp
+    buf = buffer_for(w)
+    (sb,) = symbufs(buf, w, 1)
+    assert sb.views.shape == (R, E + B, H, Hp)
+    assert sb.home.shape == (E, H, Hp) and sb.slots.shape == (R, B, H, Hp)
+    assert sb.physical_bytes == (E + R * B) * H * Hp * 2
+    assert sb.row_bytes == H * Hp * 2
+    synth.expert_weights_device(w, 0, sb.home)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    sb.slots.copy_(torch.randn((R, B, H, Hp), generator=g, device="cuda").to(torch.bfloat16))
+    torch.cuda.synchronize()
+    for d in range(R):
+        assert same(sb.views[d, :E], sb.home), d
+        assert same(sb.views[d, E:], sb.slots[d]), d
+    # a write through one rank's view is seen through the home range and every view
+    before = sb.views[1, E + 1].clone()
+    sb.views[3, 5].fill_(1.5)
+    sb.views[2, E + 1].fill_(-2.0)
+    torch.cuda.synchronize()
+    assert bool((sb.home[5] == 1.5).all())
+    for d in range(R):
+        assert bool((sb.views[d, 5] == 1.5).all()), d
+    assert bool((sb.slots[2, 1] == -2.0).all())
+    assert same(sb.views[1, E + 1], before)          # other ranks' slots are their own
+    del sb
+    buf.destroy()
+
+
+@pytest.mark.parametrize("target", [2.0, "adv"])
+def test_prefetch_views_matches_oracle_plan(target):
+    w = synth.WORKLOADS["mid_r8_s1024_k4_e32"]
+    log(f"prefetch views {w.name} target={target}")
+    topk, _ = synth.routing(w, target)
+    p = oracle.plan(topk, w.E, w.B, w.token_padding)
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    sbs = filled_weights(buf, w)
+    buf.prefetch_weight_views(plan, [sb.views for sb in sbs])
+    torch.cuda.synchronize()
+    for i, sb in enumerate(sbs):
+        for d in range(w.R):
+            for j in range(w.B):
+                e = p.prefetch_src[d, j]
+                if e >= 0:
+                    assert same(sb.views[d, w.E + j], sb.home[e]), (i, d, j)
+                else:
+                    assert bool((bits(sb.slots[d, j]) == 0x7F7F).all()), (i, d, j)
+    del sbs
+    buf.destroy()
+
+
+@pytest.mark.parametrize("name,target", [("mid_r8_s1024_k4_e32", 2.0),
+                                         ("mid_r8_s1024_k4_e32", "adv")])
+def test_ffn_views_equal_split_and_plain(name, target):
+    w = synth.WORKLOADS[name]
+    log(f"ffn views {name} target={target}")
+    topk, rw = synth.routing(w, target)
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    x_nvs, _ = buf.dispatch(plan, dev_bf16(synth.hidden(w)), dev(rw))
+    sbs = filled_weights(buf, w)
+    views = [sb.views for sb in sbs]
+    buf.prefetch_weight_views(plan, views)
+    home_plain = [sb.home.clone() for sb in sbs]
+    pool_plain = [sb.slots.clone() for sb in sbs]
+    zeros = lambda: torch.zeros((w.R, buf.NvS, w.H), dtype=torch.bfloat16, device="cuda")
+    y_views, y_split, y_plain = zeros(), zeros(), zeros()
+    buf.expert_ffn_views(plan, x_nvs, views, y_nvs=y_views)
+    buf.expert_ffn(plan, x_nvs, [sb.home for sb in sbs], [sb.slots for sb in sbs], y_nvs=y_split)
+    buf.expert_ffn(plan, x_nvs, home_plain, pool_plain, y_nvs=y_plain)
+    torch.cuda.synchronize()
+    assert bool((bits(y_views) != 0).any())
+    assert same(y_views, y_split)
+    assert same(y_views, y_plain)
+    # one rank at a time
+    y_r = zeros()
+    for d in range(w.R):
+        buf.expert_ffn_views(plan, x_nvs, views, y_nvs=y_r, rank=d)
+    torch.cuda.synchronize()
+    assert same(y_r, y_views)
+    del sbs, views
+    buf.destroy()
+
+
+def test_ffn_bwd_views_equal_plain():
+    w = synth.WORKLOADS["bwd_r8_s1024_k4_e32"]
+    log(f"ffn bwd views {w.name}")
+    topk, rw = synth.routing(w, 2.0)
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    x_nvs, _ = buf.dispatch(plan, dev_bf16(synth.hidden(w)))
+    dy_nvs, _ = buf.dispatch(plan, dev_bf16(synth.grad_out(w, w.H)))
+    sbs = filled_weights(buf, w)
+    views = [sb.views for sb in sbs]
+    buf.prefetch_weight_views(plan, views)
+    home_plain = [sb.home.clone() for sb in sbs]
+    pool_plain = [sb.slots.clone() for sb in sbs]
+
+    def run(fn, *wts):
+        outs = [torch.zeros((w.R, buf.NvS, W), dtype=torch.bfloat16, device="cuda")
+                for W in (w.Hp, w.Hp, w.Hp, w.H)]
+        fn(plan, x_nvs, dy_nvs, *wts, *outs)
+        return outs
+
+    a = run(buf.expert_ffn_bwd_views, views)
+    b = run(buf.expert_ffn_bwd, home_plain, pool_plain)
+    torch.cuda.synchronize()
+    for k, (u, v) in enumerate(zip(a, b)):
+        assert bool((bits(u) != 0).any()), k
+        assert same(u, v), k
+    del sbs, views
+    buf.destroy()
+
+
+def test_gradient_symbuf_wgrad_and_reduce():
+    w = synth.WORKLOADS["bwd_r8_s1024_k4_e32"]
+    log(f"gradient symbuf {w.name}")
+    topk, _ = synth.routing(w, 2.0)
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    x_nvs, _ = buf.dispatch(plan, dev_bf16(synth.hidden(w)))
+    dg_nvs, _ = buf.dispatch(plan, dev_bf16(synth.grad_out(w, w.Hp)))
+    gsb = symbufs(buf, w, 3, torch.float32)
+    g = torch.Generator(device="cuda").manual_seed(9)
+    for sb in gsb:
+        sb.home.copy_(torch.randn(sb.home.shape, generator=g, device="cuda"))
+        sb.slots.zero_()
+    gh_plain = [sb.home.clone() for sb in gsb]
+    rb_plain = [sb.slots.clone() for sb in gsb]
+    for i in range(3):
+        buf.expert_wgrad(plan, x_nvs, dg_nvs, gsb[i].home, gsb[i].slots)
+        buf.expert_wgrad(plan, x_nvs, dg_nvs, gh_plain[i], rb_plain[i])
+    torch.cuda.synchronize()
+    used = plan.prefetch_src.cpu().numpy().reshape(w.R, w.B) >= 0
+    assert used.any()
+    for i in range(3):
+        assert same(gsb[i].home, gh_plain[i]) and same(gsb[i].slots, rb_plain[i]), i
+        for d in range(w.R):
+            assert same(gsb[i].views[d, w.E:], gsb[i].slots[d]), (i, d)
+            assert same(gsb[i].views[d, :w.E], gsb[i].home), (i, d)
+    buf.reduce_grad(plan, [sb.home for sb in gsb], [sb.slots for sb in gsb])
+    buf.reduce_grad(plan, gh_plain, rb_plain)
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert same(gsb[i].home, gh_plain[i]), i
+        for d in range(w.R):
+            for j in range(w.B):
+                if used[d, j]:
+                    assert bool((gsb[i].views[d, w.E + j] == 0).all()), (i, d, j)
+    del gsb
+    buf.destroy()
+
+
+def test_ffn_views_full_size():
+    """The headline shape: 8 views of 288 rows of 28 MiB per projection
+    (63 GiB of address space each), row offsets past 2^32 elements."""
+    w = synth.WORKLOADS["fwd_r8_s4096_k8_e256"]
+    log(f"ffn views full size {w.name}")
+    topk, rw = synth.routing(w, "adv")
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    x_nvs, _ = buf.dispatch(plan, dev_bf16(synth.hidden(w)), dev(rw))
+    sbs = filled_weights(buf, w)
+    views = [sb.views for sb in sbs]
+    buf.prefetch_weight_views(plan, views)
+    p = np.asarray(plan.prefetch_src.cpu()).reshape(w.R, w.B)
+    for d in range(w.R):
+        for j in np.nonzero(p[d] >= 0)[0][:2]:
+            assert same(sbs[0].views[d, w.E + j], sbs[0].home[p[d, j]]), (d, j)
+    y_views = torch.zeros((w.R, buf.NvS, w.H), dtype=torch.bfloat16, device="cuda")
+    y_split = torch.zeros_like(y_views)
+    z = torch.empty((w.R, buf.NvS, w.Hp), dtype=torch.bfloat16, device="cuda")
+    buf.expert_ffn_views(plan, x_nvs, views, z_ws=z, y_nvs=y_views)
+    buf.expert_ffn(plan, x_nvs, [sb.home for sb in sbs], [sb.slots for sb in sbs], z_ws=z,
+                   y_nvs=y_split)
+    torch.cuda.synchronize()
+    assert same(y_views, y_split)
+    del sbs, views
+    buf.destroy()
