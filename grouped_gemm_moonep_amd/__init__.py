@@ -348,17 +348,19 @@ class SymmetricBuffer:
     slots [R,B,H,Hp]:   the slot chunks (pool[p] / the [R,B] reduce view)
 
     The three tensors alias the same physical memory.  They do not own it:
-    drop them before destroy()."""
+    drop them before destroy().  `slots_from`: another SymmetricBuffer whose
+    slot chunks this one maps (one prefetch pool shared by every layer)."""
 
-    def __init__(self, buf, dtype=torch.bfloat16):
+    def __init__(self, buf, dtype=torch.bfloat16, slots_from=None):
         elem = {torch.bfloat16: 2, torch.float32: 4}.get(dtype)
         if elem is None:
             raise TypeError("SymmetricBuffer holds bf16 weights or fp32 gradients")
         self._b = ctypes.c_void_p()
         dev = buf.device if buf.device.index is not None else \
             torch.device("cuda", torch.cuda.current_device())
+        share = slots_from._b if slots_from is not None else None
         with torch.cuda.device(dev):
-            _abi.check(lib().moonep_symbuf_create(buf._h, elem, ctypes.byref(self._b)),
+            _abi.check(lib().moonep_symbuf_create(buf._h, elem, share, ctypes.byref(self._b)),
                        "moonep_symbuf_create")
         info = _abi.MoonepSymbufInfo()
         _abi.check(lib().moonep_symbuf_info(self._b, ctypes.byref(info)), "moonep_symbuf_info")

@@ -79,7 +79,7 @@ def lib():
         "moonep_reduce_grad": (i32, [vp, ctypes.POINTER(MoonepPlan), P3, P3, vp]),
         "moonep_read_stats": (i32, [vp, ctypes.POINTER(MoonepPlan), vp, vp]),
         "moonep_vmm_granularity": (i32, [ctypes.POINTER(i64)]),
-        "moonep_symbuf_create": (i32, [vp, i32, ctypes.POINTER(vp)]),
+        "moonep_symbuf_create": (i32, [vp, i32, vp, ctypes.POINTER(vp)]),
         "moonep_symbuf_info": (i32, [vp, ctypes.POINTER(MoonepSymbufInfo)]),
         "moonep_symbuf_destroy": (i32, [vp]),
         "moonep_prefetch_weight_views": (i32, [vp, ctypes.POINTER(MoonepPlan), P3, vp]),

@@ -12,9 +12,14 @@
 //   home  [E]:      the home chunks in rank order;
 //   slots [R][B]:   the slot chunks in rank order.
 // Every home chunk is therefore mapped R+1 times and every slot chunk twice,
-// so the buffer costs E + R*B rows of HBM whatever the number of views.
+// so the buffer costs E + R*B rows of HBM whatever the number of views.  A
+// symbuf may instead map the slot chunks of another one (the prefetch pool
+// is one process-wide allocation shared by every layer): it then adds only
+// E rows, and the shared chunks live until the last symbuf mapping them is
+// destroyed.
 #include <stdlib.h>
 
+#include <memory>
 #include <new>
 #include <vector>
 
@@ -29,13 +34,22 @@ struct Mapping {
   size_t size;
 };
 
+// Physical chunks, released when the last symbuf holding them lets go.
+struct Chunks {
+  std::vector<hipMemGenericAllocationHandle_t> h;
+  ~Chunks() {
+    for (auto x : h) hipMemRelease(x);
+  }
+};
+
 }  // namespace
 
 struct moonep_symbuf {
   int device = 0;
   int R = 0, E = 0, B = 0, L = 0;
   size_t row_bytes = 0, gran = 0;
-  std::vector<hipMemGenericAllocationHandle_t> home_chunks, slot_chunks;
+  bool own_slots = true;
+  std::shared_ptr<Chunks> home_chunks, slot_chunks;
   std::vector<Mapping> maps;
   std::vector<Mapping> ranges;   // reservations
   char* views = nullptr;
@@ -60,12 +74,10 @@ static hipError_t release(moonep_symbuf* b) {
   };
   for (const Mapping& m : b->maps) keep(hipMemUnmap(m.va, m.size));
   for (const Mapping& r : b->ranges) keep(hipMemAddressFree(r.va, r.size));
-  for (auto h : b->home_chunks) keep(hipMemRelease(h));
-  for (auto h : b->slot_chunks) keep(hipMemRelease(h));
   b->maps.clear();
   b->ranges.clear();
-  b->home_chunks.clear();
-  b->slot_chunks.clear();
+  b->home_chunks.reset();
+  b->slot_chunks.reset();
   return err;
 }
 
@@ -102,10 +114,13 @@ moonep_status_t moonep_vmm_granularity(int64_t* out) {
 }
 
 moonep_status_t moonep_symbuf_create(moonep_handle_t h, int32_t elem_bytes,
-                                     moonep_symbuf_t* out) {
+                                     moonep_symbuf_t slots_from, moonep_symbuf_t* out) {
   if (!h || !out || (elem_bytes != 2 && elem_bytes != 4)) return MOONEP_ERR_ARG;
   *out = nullptr;
   const Dims& d = h->c.d;
+  if (slots_from && (slots_from->R != d.R || slots_from->B != d.B ||
+                     slots_from->row_bytes != (size_t)d.H * d.Hp * elem_bytes))
+    return MOONEP_ERR_ARG;
   moonep_symbuf* b = new (std::nothrow) moonep_symbuf;
   if (!b) return MOONEP_ERR_NOMEM;
   b->R = d.R; b->E = d.E; b->B = d.B; b->L = d.L;
@@ -127,16 +142,23 @@ moonep_status_t moonep_symbuf_create(moonep_handle_t h, int32_t elem_bytes,
     delete b;
     return MOONEP_ERR_CONFIG;
   }
+  if (slots_from && slots_from->device != b->device) {
+    delete b;
+    return MOONEP_ERR_ARG;
+  }
   moonep_status_t st = MOONEP_OK;
   hipError_t e = hipSuccess;
-  // physical chunks
+  // physical chunks (the slot chunks possibly another symbuf's)
+  b->home_chunks = std::make_shared<Chunks>();
+  b->slot_chunks = slots_from ? slots_from->slot_chunks : std::make_shared<Chunks>();
+  b->own_slots = !slots_from;
   for (int r = 0; r < d.R && e == hipSuccess; ++r) {
     hipMemGenericAllocationHandle_t ph;
     e = hipMemCreate(&ph, home_chunk, &prop, 0);
-    if (e == hipSuccess) b->home_chunks.push_back(ph);
-    if (e == hipSuccess && slot_chunk) {
+    if (e == hipSuccess) b->home_chunks->h.push_back(ph);
+    if (e == hipSuccess && slot_chunk && !slots_from) {
       e = hipMemCreate(&ph, slot_chunk, &prop, 0);
-      if (e == hipSuccess) b->slot_chunks.push_back(ph);
+      if (e == hipSuccess) b->slot_chunks->h.push_back(ph);
     }
   }
   if (e == hipErrorOutOfMemory) st = MOONEP_ERR_NOMEM;
@@ -148,12 +170,13 @@ moonep_status_t moonep_symbuf_create(moonep_handle_t h, int32_t elem_bytes,
   for (int r = 0; r < d.R && e == hipSuccess; ++r) {
     char* view = b->views + (size_t)r * view_rows * b->row_bytes;
     for (int g = 0; g < d.R && e == hipSuccess; ++g)
-      e = map(b, view + (size_t)g * home_chunk, home_chunk, b->home_chunks[g]);
+      e = map(b, view + (size_t)g * home_chunk, home_chunk, b->home_chunks->h[g]);
     if (e == hipSuccess && slot_chunk)
-      e = map(b, view + (size_t)d.E * b->row_bytes, slot_chunk, b->slot_chunks[r]);
-    if (e == hipSuccess) e = map(b, b->home + (size_t)r * home_chunk, home_chunk, b->home_chunks[r]);
+      e = map(b, view + (size_t)d.E * b->row_bytes, slot_chunk, b->slot_chunks->h[r]);
+    if (e == hipSuccess)
+      e = map(b, b->home + (size_t)r * home_chunk, home_chunk, b->home_chunks->h[r]);
     if (e == hipSuccess && slot_chunk)
-      e = map(b, b->slots + (size_t)r * slot_chunk, slot_chunk, b->slot_chunks[r]);
+      e = map(b, b->slots + (size_t)r * slot_chunk, slot_chunk, b->slot_chunks->h[r]);
   }
   // read/write access from the device, over every fully mapped range
   hipMemAccessDesc acc = {};
@@ -176,7 +199,8 @@ moonep_status_t moonep_symbuf_info(moonep_symbuf_t b, moonep_symbuf_info_t* out)
   out->home = b->home;
   out->slots = b->slots;
   out->row_bytes = (int64_t)b->row_bytes;
-  out->physical_bytes = ((int64_t)b->E + (int64_t)b->R * b->B) * (int64_t)b->row_bytes;
+  out->physical_bytes =
+      ((int64_t)b->E + (b->own_slots ? (int64_t)b->R * b->B : 0)) * (int64_t)b->row_bytes;
   out->granularity = (int64_t)b->gran;
   return MOONEP_OK;
 }

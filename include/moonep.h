@@ -297,7 +297,8 @@ typedef struct {
   void* home;              /* device address, [E,H,Hp]                       */
   void* slots;             /* device address, [R,B,H,Hp]; NULL when B == 0   */
   int64_t row_bytes;       /* H*Hp*elem_bytes                                */
-  int64_t physical_bytes;  /* (E + R*B) * row_bytes                          */
+  int64_t physical_bytes;  /* HBM it allocated: (E + R*B) * row_bytes, or
+                              E * row_bytes when it maps another's slots     */
   int64_t granularity;     /* the device's minimum VMM granularity, bytes    */
 } moonep_symbuf_info_t;
 
@@ -307,13 +308,18 @@ moonep_status_t moonep_vmm_granularity(int64_t* out);
 
 /* Create the symbuf of one projection for the handle's configuration, on
  * the current device.  elem_bytes: 2 for bf16 weights, 4 for fp32
- * gradients.  (E/R)*H*Hp*elem_bytes and B*H*Hp*elem_bytes must be multiples
- * of the granularity (MOONEP_ERR_CONFIG otherwise).  MOONEP_ERR_NOMEM when
- * the physical memory is not there, MOONEP_ERR_HIP when another VMM call
- * fails; on any error nothing stays allocated.  The symbuf does not depend
- * on the handle after this call. */
+ * gradients.  slots_from: NULL, or a symbuf of the same R, B, row size and
+ * device whose slot chunks this one maps instead of allocating its own (the
+ * README's prefetch pool, one process-wide allocation that every layer's
+ * [E+B] range shares; MOONEP_ERR_ARG if it does not match).  Shared chunks
+ * stay allocated until every symbuf that maps them is destroyed.
+ * (E/R)*H*Hp*elem_bytes and B*H*Hp*elem_bytes must be multiples of the
+ * granularity (MOONEP_ERR_CONFIG otherwise).  MOONEP_ERR_NOMEM when the
+ * physical memory is not there, MOONEP_ERR_HIP when another VMM call fails;
+ * on any error nothing stays allocated.  The symbuf does not depend on the
+ * handle after this call. */
 moonep_status_t moonep_symbuf_create(moonep_handle_t h, int32_t elem_bytes,
-                                     moonep_symbuf_t* out);
+                                     moonep_symbuf_t slots_from, moonep_symbuf_t* out);
 
 /* Addresses and sizes of a symbuf (host out). */
 moonep_status_t moonep_symbuf_info(moonep_symbuf_t b, moonep_symbuf_info_t* out);

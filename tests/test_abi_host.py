@@ -100,7 +100,7 @@ def test_null_arguments_rejected_on_host():
     assert lib.moonep_read_stats(None, ctypes.byref(plan), None, None) == ERR
     assert lib.moonep_vmm_granularity(None) == ERR
     out = ctypes.c_void_p()
-    assert lib.moonep_symbuf_create(None, 2, ctypes.byref(out)) == ERR
+    assert lib.moonep_symbuf_create(None, 2, None, ctypes.byref(out)) == ERR
     assert lib.moonep_symbuf_info(None, None) == ERR
     assert lib.moonep_symbuf_destroy(None) == _abi.MOONEP_OK
     assert lib.moonep_prefetch_weight_views(None, ctypes.byref(plan), P3(), None) == ERR

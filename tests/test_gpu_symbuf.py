@@ -83,6 +83,40 @@ def test_views_alias_home_and_slots():
     buf.destroy()
 
 
+def test_layers_share_one_prefetch_pool():
+    """Two layers' weight buffers mapping one set of slot chunks (the README's
+    process-wide prefetch pool): a slot written through one layer's view is
+    read through the other's, each layer keeps its own home rows, the second
+    allocates only E rows, and the pool outlives the symbuf that created it."""
+    from grouped_gemm_moonep_amd import SymmetricBuffer
+    w = synth.WORKLOADS["mid_r8_s1024_k4_e32"]
+    E, B = w.E, w.B
+    buf = buffer_for(w)
+    (l0,) = symbufs(buf, w, 1)
+    l1 = SymmetricBuffer(buf, slots_from=l0)
+    assert l1.physical_bytes == E * l0.row_bytes
+    assert l0.physical_bytes == (E + w.R * B) * l0.row_bytes
+    l0.home.fill_(1.0)
+    l1.home.fill_(2.0)
+    l0.views[4, E + 2].fill_(3.0)
+    torch.cuda.synchronize()
+    assert bool((l1.views[4, E + 2] == 3.0).all()) and bool((l1.slots[4, 2] == 3.0).all())
+    assert bool((l1.views[4, :E] == 2.0).all()) and bool((l0.views[4, :E] == 1.0).all())
+    l0.destroy()
+    l1.views[5, E + 3].fill_(4.0)
+    torch.cuda.synchronize()
+    assert bool((l1.slots[5, 3] == 4.0).all()) and bool((l1.views[4, E + 2] == 3.0).all())
+    l1.destroy()
+    from grouped_gemm_moonep_amd import MoonepError
+    other = buffer_for(synth.WORKLOADS["tiny_r4_s64_k2_e8"])
+    l2 = SymmetricBuffer(other)
+    with pytest.raises(MoonepError):
+        SymmetricBuffer(buf, slots_from=l2)          # another R, B and row size
+    l2.destroy()
+    other.destroy()
+    buf.destroy()
+
+
 @pytest.mark.parametrize("target", [2.0, "adv"])
 def test_prefetch_views_matches_oracle_plan(target):
     w = synth.WORKLOADS["mid_r8_s1024_k4_e32"]
