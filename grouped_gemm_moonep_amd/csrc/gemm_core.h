@@ -31,9 +31,10 @@
 // buffer loads (no staging registers, no LDS write instructions); weights are
 // fetched two steps ahead, activations one.  Operands contiguous along K are
 // kept as 128-byte rows (whole cache lines per load) with an XOR chunk
-// swizzle and read with ds_read_b128; operands stored [k][n] (gate/up
-// weights, both weight-gradient operands) are kept as 256-byte k-rows and read
-// with the gfx950 transposing LDS read (ds_read_b64_tr_b16), which hands each
+// swizzle that keeps 16 consecutive rows on distinct LDS banks, and read with
+// ds_read_b128; operands stored [k][n] (gate/up weights, both weight-gradient
+// operands) are kept as 256-byte k-rows and read with the gfx950 transposing
+// LDS read (ds_read_b64_tr_b16), which hands each
 // lane one column's 4 consecutive k.  Fragments are double-buffered in
 // registers and every load and fragment read is slotted between MFMAs, so the
 // matrix unit stays busy across the one barrier per step.  Buffer descriptors
@@ -130,10 +131,15 @@ __device__ __forceinline__ void bstore16(Rsrc r, uint32_t voff, unsigned v) {
 // per ring slot.
 //
 // Row tile (operand contiguous along k): rows of 128 B (64 k); the 16-byte
-// chunk c of row r sits at position c ^ (r & 7), so the 8 rows read together
-// by an MFMA fragment load hit 8 distinct bank groups.  One LDS-DMA load (a
-// wave, 1 KiB) fills 8 rows, each a whole 128-byte cache line: the L1/L2 path
-// costs per cache line touched, and half-line rows would halve its rate.
+// chunk c of row r sits at position c ^ ((r >> 1) & 7).  The LDS serves 256
+// bytes per clock, i.e. 16 lanes of a 16-byte fragment read, which here are
+// 16 consecutive rows at the same chunk: two rows share each 256-byte window
+// and the swizzle sends all 16 to distinct 16-byte bank groups (measured:
+// no bank conflicts, where c ^ (r & 7) doubles the read time).  One LDS-DMA
+// load (a wave, 1 KiB) fills 8 rows, each a whole 128-byte cache line: the
+// L1/L2 path costs per cache line touched, and half-line rows would halve its
+// rate.  Rows 8 apart differ in bit 2 of the swizzle, so even and odd loads
+// of a wave use two lane offsets.
 //
 // Column tile (operand stored [k][n], n contiguous): two regions of 128
 // columns (gate and up weights, or two column halves of one matrix), 64 k
@@ -150,23 +156,27 @@ struct RowTileT {
   static constexpr bool kRows = true;
   static constexpr int kLoads = NL;
   DmaRsrc rs;
-  uint32_t voff;        // this lane's offset for load 0 of k-block 0
+  uint32_t voff[2];     // this lane's offsets for even / odd loads of k-block 0
   uint32_t step;        // byte distance between consecutive loads of a wave (8 rows)
+  __device__ __forceinline__ static int swz(int r) { return (r >> 1) & 7; }
   // base: row 0, k 0 of the tile; ld: row stride (elements).  Rows at or
   // past rows_valid lie outside the descriptor's range and read zero.
   __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int rows_valid) {
     const int w = wave_id(), lane = threadIdx.x & 63;
     rs = make_dma_rsrc(base, (int64_t)rows_valid * ld * 2);
+    // lane -> LDS row r + 8 i (load i), position lane & 7, which holds the
+    // global chunk (lane & 7) ^ swz(r + 8 i) = (lane & 7) ^ swz(r) ^ 4 (i & 1)
     const int r = 8 * NL * w + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
-    voff = (uint32_t)(r * ld * 2 + c * 16);
+    const int c = (lane & 7) ^ swz(r);
+    voff[0] = (uint32_t)(r * ld * 2 + c * 16);
+    voff[1] = (uint32_t)(r * ld * 2 + (c ^ 4) * 16);
     step = (uint32_t)(16 * ld);
   }
   __device__ __forceinline__ uint32_t koff(int64_t k0) const { return (uint32_t)(k0 * 2); }
   // load i (0..NL-1) of this wave for the k-block at byte offset ko
   __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t ko, bool valid) const {
     const uint32_t s = __builtin_amdgcn_readfirstlane(valid ? ko + (uint32_t)i * step : kOob);
-    load_lds(rs, tile + (wave_id() * NL + i) * 1024, voff + s);
+    load_lds(rs, tile + (wave_id() * NL + i) * 1024, voff[i & 1] + s);
   }
   __device__ __forceinline__ void issue(lds_t* tile, int64_t k0, bool valid) const {
 #pragma unroll
@@ -174,7 +184,7 @@ struct RowTileT {
   }
   // 8 consecutive k (sub-step kk of 4, lane half lh) of tile row `row`
   __device__ __forceinline__ static bf16x8 frag(const lds_t* tile, int row, int kk, int lh) {
-    const int c = (2 * kk + lh) ^ (row & 7);
+    const int c = (2 * kk + lh) ^ swz(row);
     return *(const __attribute__((address_space(3))) bf16x8*)(tile + row * 128 + c * 16);
   }
 };
