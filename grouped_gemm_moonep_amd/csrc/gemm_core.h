@@ -158,6 +158,7 @@ struct RowTileT {
   DmaRsrc rs;
   uint32_t voff[2];     // this lane's offsets for even / odd loads of k-block 0
   uint32_t step;        // byte distance between consecutive loads of a wave (8 rows)
+  uint32_t wlds;        // this wave's first 1 KiB block inside a slot
   __device__ __forceinline__ static int swz(int r) { return (r >> 1) & 7; }
   // base: row 0, k 0 of the tile; ld: row stride (elements).  Rows at or
   // past rows_valid lie outside the descriptor's range and read zero.
@@ -171,16 +172,24 @@ struct RowTileT {
     voff[0] = (uint32_t)(r * ld * 2 + c * 16);
     voff[1] = (uint32_t)(r * ld * 2 + (c ^ 4) * 16);
     step = (uint32_t)(16 * ld);
+    wlds = (uint32_t)(w * NL * 1024);
   }
   __device__ __forceinline__ uint32_t koff(int64_t k0) const { return (uint32_t)(k0 * 2); }
-  // load i (0..NL-1) of this wave for the k-block at byte offset ko
-  __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t ko, bool valid) const {
-    const uint32_t s = __builtin_amdgcn_readfirstlane(valid ? ko + (uint32_t)i * step : kOob);
-    load_lds(rs, tile + (wave_id() * NL + i) * 1024, voff[i & 1] + s);
+  // load i (0..NL-1) of this wave for the k-block at byte offset ko (kOob:
+  // the step is past the end; kOob + i step stays out of range).  The step's
+  // validity is folded into ko once and the wave's LDS block is kept from
+  // init: each load then costs two scalar adds, which the compiler can slot
+  // between MFMAs (a per-load select and wave-id computation made a burst of
+  // ~50 scalar instructions at the top of every step, with the matrix unit
+  // idle).
+  __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t ko) const {
+    const uint32_t s = ko + (uint32_t)i * step;
+    load_lds(rs, tile + wlds + i * 1024, voff[i & 1] + s);
   }
   __device__ __forceinline__ void issue(lds_t* tile, int64_t k0, bool valid) const {
+    const uint32_t ko = valid ? koff(k0) : kOob;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) issue1(tile, i, koff(k0), valid);
+    for (int i = 0; i < NL; ++i) issue1(tile, i, ko);
   }
   // 8 consecutive k (sub-step kk of 4, lane half lh) of tile row `row`
   __device__ __forceinline__ static bf16x8 frag(const lds_t* tile, int row, int kk, int lh) {
@@ -206,14 +215,17 @@ struct RowTile2 {
     t1.init(base1, ld, rows_valid);
     k1 = (uint32_t)k_first;
   }
+  // k: the step's first k, or kOob past the end (both matrices then read zero)
   __device__ __forceinline__ uint32_t koff(int64_t k0) const { return (uint32_t)k0; }
-  __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t k, bool valid) const {
-    if (k < k1) t0.issue1(tile, i, t0.koff(k), valid);
-    else t1.issue1(tile, i, t1.koff(k - k1), valid);
+  __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t k) const {
+    if (k < k1) t0.issue1(tile, i, t0.koff(k));
+    else if (k == kOob) t1.issue1(tile, i, kOob);
+    else t1.issue1(tile, i, t1.koff(k - k1));
   }
   __device__ __forceinline__ void issue(lds_t* tile, int64_t k0, bool valid) const {
+    const uint32_t k = valid ? koff(k0) : kOob;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) issue1(tile, i, koff(k0), valid);
+    for (int i = 0; i < NL; ++i) issue1(tile, i, k);
   }
   __device__ __forceinline__ static bf16x8 frag(const lds_t* tile, int row, int kk, int lh) {
     return RowTileT<NL>::frag(tile, row, kk, lh);
@@ -226,6 +238,7 @@ struct ColTile {
   DmaRsrc rs;           // this wave's region (waves 0,1: region 0; waves 2,3: region 1)
   uint32_t voff;        // this lane's offset for load 0 of k-block 0 (out of range past nv)
   uint32_t ld2;
+  uint32_t wlds;        // this wave's first 1 KiB block inside a slot
   // src0/src1: k 0, n 0 of the two 128-column regions; ld: k stride
   // (elements); k_total: valid k rows from k 0; nv0/nv1: valid columns
   __device__ __forceinline__ void init(const uint16_t* src0, const uint16_t* src1, int64_t ld,
@@ -237,15 +250,18 @@ struct ColTile {
     const int k = 32 * (w & 1) + (lane >> 4);        // load i adds 4 i rows
     const int col = 8 * ((lane & 15) ^ (4 * (k & 3)));
     voff = col < (region ? nv1 : nv0) ? (uint32_t)(k * ld * 2 + col * 2) : kOob;
+    wlds = (uint32_t)(w * 8 * 1024);
   }
   __device__ __forceinline__ uint32_t koff(int64_t k0) const { return (uint32_t)(k0 * ld2); }
-  __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t ko, bool valid) const {
-    const uint32_t s = __builtin_amdgcn_readfirstlane(valid ? ko + (uint32_t)(4 * i) * ld2 : kOob);
-    load_lds(rs, tile + (wave_id() * 8 + i) * 1024, voff + s);
+  // ko: the step's byte offset, or kOob past the end
+  __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t ko) const {
+    const uint32_t s = ko + (uint32_t)(4 * i) * ld2;
+    load_lds(rs, tile + wlds + i * 1024, voff + s);
   }
   __device__ __forceinline__ void issue(lds_t* tile, int64_t k0, bool valid) const {
+    const uint32_t ko = valid ? koff(k0) : kOob;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) issue1(tile, i, koff(k0), valid);
+    for (int i = 0; i < 8; ++i) issue1(tile, i, ko);
   }
   // 8 consecutive k (sub-step kk of 4, lane half lh) of tile column n (the lane's)
   __device__ __forceinline__ static bf16x8 frag(const lds_t* tile, int nb, int kk, int lh) {
@@ -364,8 +380,8 @@ __device__ __forceinline__ void kstep(const TA& la, const TB& lb, const Ring& ri
   const lds_t* Bn = ring.b<J1>();
   lds_t* la_dst = ring.a<J1>();
   lds_t* lb_dst = ring.b<J2>();
-  const uint32_t koa = la.koff((int64_t)(j + 1) * BK), kob = lb.koff((int64_t)(j + 2) * BK);
-  const bool va = j + 1 < nk, vb = j + 2 < nk;
+  const uint32_t koa = j + 1 < nk ? la.koff((int64_t)(j + 1) * BK) : kOob;
+  const uint32_t kob = j + 2 < nk ? lb.koff((int64_t)(j + 2) * BK) : kOob;
   MOONEP_PIN();
 #pragma unroll
   for (int p = 0; p < P; ++p) {
@@ -373,8 +389,8 @@ __device__ __forceinline__ void kstep(const TA& la, const TB& lb, const Ring& ri
     mma1<MI>(acc, (sub & 1) ? f1 : f0, idx);
     if (sub < 3 && idx < NF)
       read_frag<MI, TA, TB>((sub & 1) ? f0 : f1, idx, A, Bt, sub + 1, arow0, nrow);
-    if (p % 3 == 1 && p / 3 < NA) la.issue1(la_dst, p / 3, koa, va);
-    if (p >= B0 && (p - B0) % BS == 0 && (p - B0) / BS < NB) lb.issue1(lb_dst, (p - B0) / BS, kob, vb);
+    if (p % 3 == 1 && p / 3 < NA) la.issue1(la_dst, p / 3, koa);
+    if (p >= B0 && (p - B0) % BS == 0 && (p - B0) / BS < NB) lb.issue1(lb_dst, (p - B0) / BS, kob);
     if (p == BAR) {
       MOONEP_PIN();
       wait_loads<kLoadsPerStep>();
