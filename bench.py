@@ -317,6 +317,63 @@ def time_views(w, buf, batches, home, pool, x, steps):
             "note": "per-rank [E+B] views on hipMemMap'd chunks vs separate home/pool tensors"}
 
 
+def time_graph(w, buf, batches, home, pool, x, steps):
+    """The forward step (plan, dispatch, prefetch, FFN, combine) captured once
+    as a HIP graph and replayed with each batch's routing copied into the
+    captured input, beside the same step launched eagerly: the path has no
+    host synchronisation and static shapes, so one graph serves every
+    routing."""
+    import torch
+    dev = x.device
+    plan = buf.new_plan()
+    topk_in = torch.empty_like(batches[0][1])
+    rw_in = torch.empty_like(batches[0][2])
+    x_nvs = torch.empty((w.R, buf.NvS, w.H), dtype=torch.bfloat16, device=dev)
+    rw_nvs = torch.empty((w.R, buf.NvS), dtype=torch.float32, device=dev)
+    z = torch.empty((w.R, buf.NvS, w.Hp), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((w.R, w.S, w.H), dtype=torch.bfloat16, device=dev)
+    rw_sk = torch.empty((w.R, w.S, w.K), dtype=torch.float32, device=dev)
+
+    def step():
+        buf.plan(topk_in, plan=plan)
+        buf.dispatch(plan, x, rw_in, x_nvs=x_nvs, rw_nvs=rw_nvs)
+        buf.prefetch_weight(plan, home, pool)
+        buf.expert_ffn(plan, x_nvs, home, pool, z_ws=z, y_nvs=x_nvs)
+        buf.combine(plan, x_nvs, rw_nvs, out=out, rw_sk=rw_sk)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    res = {}
+    for mode in ("eager", "graph", "eager", "graph"):
+        t_total = 0.0
+        for i in range(steps):
+            _, topk, rw = batches[i % len(batches)]
+            topk_in.copy_(topk)
+            rw_in.copy_(rw)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            if mode == "graph":
+                g.replay()
+            else:
+                step()
+            torch.cuda.synchronize()
+            t_total += time.perf_counter() - t0
+        res[mode] = t_total / steps           # the second pass of each mode is kept
+    del g
+    return {"eager_ms": round(res["eager"] * 1e3, 3), "graph_ms": round(res["graph"] * 1e3, 3),
+            "graph_over_eager": round(res["graph"] / res["eager"], 4), "steps": steps,
+            "note": "host wall clock per step (launch to completion), inputs copied in "
+                    "before each timed step"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,6 +392,9 @@ def main():
     ap.add_argument("--overlap", action="store_true",
                     help="also time two pipelined micro-batches with dispatch/combine on a "
                          "second stream at a 32-CU budget against running them back to back")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the forward step as one HIP graph replayed for every "
+                         "routing beside the same step launched eagerly")
     ap.add_argument("--views", action="store_true",
                     help="also time prefetch and the FFN over per-rank [E+B] views on virtual "
                          "memory (SymmetricBuffer) beside ordinary home/pool tensors; needs "
@@ -532,6 +592,9 @@ def main():
         "combine_us_copy_mode": round((t_comb + t_copy) * 1e6, 1),
         "note": f"one copy of the used slots (real + padding rows) per call, timed at maxvio {t_last}"}
     del scratch
+
+    if args.graph:
+        result["graph"] = time_graph(w, buf, batches, home, pool, x, max(3, args.steps))
 
     if args.views:
         result["views"] = time_views(w, buf, batches, home, pool, x, max(2, args.steps // 2))
