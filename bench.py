@@ -48,6 +48,36 @@ def alg_bytes(w):
     return plan, dispatch, combine
 
 
+def ffn_bytes(w, plan):
+    """Algorithmic HBM bytes of one ffn_gateup and one ffn_down launch for a
+    plan: every used (rank, weight row) pair's weights once, every row of the
+    ranks' segments (padding included) read once and its output written once."""
+    EB = w.E + w.B
+    seg = plan.arrays["seg_tokens"].cpu().numpy().reshape(w.R, EB)
+    cu = plan.arrays["cu_seqlens"].cpu().numpy().reshape(w.R, EB)
+    pairs = int((seg > 0).sum())
+    rows = int(cu[:, -1].sum())
+    wrow = w.H * w.Hp * 2
+    return {"gateup_bytes": pairs * 2 * wrow + rows * (w.H + w.Hp) * 2,
+            "down_bytes": pairs * wrow + rows * (w.Hp + w.H) * 2}
+
+
+def ffn_roofline(name, flops, nbytes, t):
+    """The binding roofline of a GEMM launch: HBM when its arithmetic intensity
+    is below the machine balance (bf16 peak over HBM peak), MFMA otherwise."""
+    hbm = flops / nbytes < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if hbm:
+        ach = nbytes / t / 1e9
+        r = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+             "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = flops / t / 1e12
+        r = {"kernel": name, "bound": "mfma", "achieved": round(ach, 1),
+             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+    r["per_launch"] = {"flops": flops, "bytes": nbytes, "avg_s": t}
+    return r
+
+
 def ffn_flops(w):
     """Algorithmic flops of the grouped FFN over every real slot (padding rows
     not counted): gate and up 2*H*H' each, down 2*H*H' per slot."""
@@ -483,6 +513,7 @@ def main():
         st = buf.read_stats(plan)
         stats[t] = {"dups": int(st[1]), "maxvio": float(np.int32(st[5]).view(np.float32)),
                     "pad_rows": int(st[4])}
+        stats[t].update(ffn_bytes(w, plan))
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
@@ -537,6 +568,9 @@ def main():
             sweep[k]["ffn_over_first"] = round(sweep[k]["ffn_ms"] / sweep[t0]["ffn_ms"], 3)
             sweep[k]["pdc_over_first"] = round(sweep[t0]["pdc_GBps"] / sweep[k]["pdc_GBps"], 3)
 
+    # algorithmic FFN bytes averaged over the timed steps (each step's plan)
+    gu_bytes = float(np.mean([stats[u]["gateup_bytes"] for u in used]))
+    dn_bytes = float(np.mean([stats[u]["down_bytes"] for u in used]))
     result = {
         "metric": "plan+dispatch+combine GB/s, grouped-GEMM TFLOP/s vs maxvio, 1 rank",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -549,17 +583,12 @@ def main():
                    "step": f"plan, dispatch, prefetch_weight, expert_gateup + expert_down "
                            f"({w.R} ranks), combine"},
         "gemm_tflops": round(tflops, 1),
-        "roofline": {"kernel": "ffn_gateup (gate and up GEMMs + SwiGLU, all 8 ranks, one launch)",
-                     "bound": "mfma", "achieved": round(gateup_flops(w) / t_gu / 1e12, 1),
-                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gateup_flops(w) / t_gu / 1e12 / BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic() if w.name == WORKLOAD else None,
-                     "per_launch": {"flops": gateup_flops(w), "avg_s": t_gu}},
-        "roofline_down": {"kernel": "ffn_down (down GEMM, all 8 ranks, one launch)",
-                          "bound": "mfma", "achieved": round(down_flops(w) / t_dn / 1e12, 1),
-                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                          "frac": round(down_flops(w) / t_dn / 1e12 / BF16_PEAK_TFLOPS, 4),
-                          "traffic": None, "per_launch": {"flops": down_flops(w), "avg_s": t_dn}},
+        "roofline": {**ffn_roofline(
+            f"ffn_gateup (gate and up GEMMs + SwiGLU, all {w.R} ranks, one launch)",
+            gateup_flops(w), gu_bytes, t_gu),
+            "traffic": measured_traffic() if w.name == WORKLOAD else None},
+        "roofline_down": {**ffn_roofline(f"ffn_down (down GEMM, all {w.R} ranks, one launch)",
+                                         down_flops(w), dn_bytes, t_dn), "traffic": None},
         "roofline_dispatch": {"bound": "hbm", "achieved": round(db / t_disp / 1e9, 1),
                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(db / t_disp / 1e9 / HBM_PEAK_GBS, 4),
