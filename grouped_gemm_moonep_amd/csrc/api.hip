@@ -214,9 +214,7 @@ moonep_status_t moonep_plan(moonep_handle_t h, const int32_t* topk,
                             const moonep_plan_t* plan, hipStream_t stream) {
   if (!h || !topk || !aligned(topk, 4) || !plan_ok(plan)) return MOONEP_ERR_ARG;
   if (tokens_per_expert && !aligned(tokens_per_expert, 4)) return MOONEP_ERR_ARG;
-  hipError_t e = launch_plan(h->c, topk, tokens_per_expert, *plan, stream);
-  if (e == hipSuccess) e = launch_gemm_schedule(h->c, *plan, stream);
-  return hip_status(e);
+  return hip_status(launch_plan(h->c, topk, tokens_per_expert, *plan, stream));
 }
 
 moonep_status_t moonep_dispatch(moonep_handle_t h, const moonep_plan_t* plan,

@@ -16,8 +16,9 @@
 // projection stored [H,H'].
 //
 // Kernels (all on the caller's stream):
-//   gemm.hip       gemm_schedule (one workgroup per rank: M-tiles of <= 256
-//                  rows, never crossing a segment), ffn_gateup (256 x (128
+//   tile_schedule.h the M-tiles of each rank (<= 256 rows, never crossing a
+//                  segment), built by the planner's last kernel;
+//   gemm.hip       ffn_gateup (256 x (128
 //                  gate + 128 up), K = H, fused SwiGLU writing Z), ffn_down
 //                  (256 x 256 of Y = Z Wd^T, K = H');
 //   gemm_bwd.hip   ffn_bwd_dz, ffn_bwd_gu, ffn_bwd_dx (the FFN backward) and
@@ -45,6 +46,7 @@
 #pragma once
 
 #include "internal.h"
+#include "tile_schedule.h"
 
 namespace moonep {
 namespace {
@@ -58,7 +60,8 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
 constexpr int BM = 256, BN = 256, BK = 64;        // K advances 64 per step
-constexpr int kHalfTileM = 128;                   // rows of a segment's short last tile
+constexpr int kHalfTileM = kShortTileM;           // rows of a segment's short last tile
+static_assert(BM == kTileM && kGemmTileM == kTileM, "one M-tile height everywhere");
 constexpr int kXcds = 8;
 constexpr int kLoadsPerStep = 8;                  // LDS-DMA loads per wave per tile and step
 constexpr int kTileOffB = 0;                      // B tile offset inside its slot
@@ -525,8 +528,6 @@ __device__ __forceinline__ const uint16_t* weight_row(const FfnArgs& a, int p, i
 // group start * 16 + group size); the workgroups of a group starting at tile
 // g with size n are those with index l in [g ntn, (g + n) ntn), so l / ntn is
 // a tile of the same group and names it.
-constexpr int kGroupM = 4;
-
 __device__ __forceinline__ bool decode(const FfnArgs& a, int* d, Tile* tl, int* nt) {
   const int64_t lt = logical_tile();
   const int64_t per_rank = (int64_t)a.max_tiles * a.ntn;

@@ -84,7 +84,6 @@ hipError_t launch_prefetch(const Ctx& c, const moonep_plan_t& p, const WeightRef
 hipError_t launch_reduce_grad(const Ctx& c, const moonep_plan_t& p,
                               float* const gh[3], float* const rb[3],
                               hipStream_t s);
-hipError_t launch_gemm_schedule(const Ctx& c, const moonep_plan_t& p, hipStream_t s);
 hipError_t launch_gateup(const Ctx& c, const moonep_plan_t& p, int rank,
                          const uint16_t* x_nvs, const WeightRef& w, uint16_t* z,
                          hipStream_t s);

@@ -27,8 +27,11 @@
 //   plan_assign (R x chunks workgroups): stable rank of each token among the
 //                earlier tokens of the same expert (popcount of the lane
 //                masks below it), its line position, piece, row and slot;
-//                padding slots get src = -1.
+//                padding slots get src = -1.  One more workgroup per rank
+//                builds that rank's grouped-GEMM tile schedule
+//                (tile_schedule.h) at the same time.
 #include "internal.h"
+#include "tile_schedule.h"
 
 namespace moonep {
 namespace {
@@ -36,7 +39,7 @@ namespace {
 constexpr int kSolveThreads = 1024;
 
 struct PlanArgs {
-  int R, S, K, E, B, L, tp, nch;
+  int R, S, K, E, B, L, tp, nch, max_tiles;
   int NvS;
   const int32_t* topk;
   const int32_t* tpe;
@@ -529,6 +532,15 @@ constexpr int kShiftLds = 4096;     // shift table staged in LDS up to R*E ints
 constexpr int kPiecesLds = 1024;    // piece table staged in LDS up to this many ints
 
 __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
+  if (blockIdx.x == a.nch) {
+    // the grid's extra column: rank blockIdx.y's grouped-GEMM tile schedule,
+    // built from plan_solve's segments alongside the token assignment
+    __shared__ int wsum[4];
+    build_tile_schedule(a.aux + a.ax.act, a.cu, a.segn, a.aux + a.ax.tiles,
+                        a.aux + a.ax.ntiles, blockIdx.y, 2 * a.L, a.E + a.B, a.tp, a.max_tiles,
+                        wsum);
+    return;
+  }
   __shared__ unsigned long long mask[4][kMaxE];
   __shared__ int s_base[kMaxE];
   __shared__ int s_shift[kShiftLds];
@@ -623,7 +635,7 @@ hipError_t launch_plan(const Ctx& c, const int32_t* topk, const int32_t* tpe,
   const Dims& d = c.d;
   PlanArgs a;
   a.R = d.R; a.S = d.S; a.K = d.K; a.E = d.E; a.B = d.B; a.L = d.L; a.tp = d.tp;
-  a.nch = d.nch; a.NvS = (int)d.NvS;
+  a.nch = d.nch; a.NvS = (int)d.NvS; a.max_tiles = d.max_tiles;
   a.topk = topk; a.tpe = tpe;
   a.cc = c.cc; a.chunk_err = c.chunk_err; a.rankpre = c.rankpre; a.shift = c.shift;
   a.pieces = c.pieces; a.npieces = c.npieces; a.line = c.line;
@@ -633,7 +645,7 @@ hipError_t launch_plan(const Ctx& c, const int32_t* topk, const int32_t* tpe,
   const dim3 grid(d.nch, d.R);
   plan_hist<<<grid, kPlanChunk, 0, s>>>(a);
   plan_solve<<<1, kSolveThreads, 0, s>>>(a);
-  plan_assign<<<grid, kPlanChunk, 0, s>>>(a);
+  plan_assign<<<dim3(d.nch + 1, d.R), kPlanChunk, 0, s>>>(a);
   return hipGetLastError();
 }
 
