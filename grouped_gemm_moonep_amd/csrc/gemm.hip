@@ -48,7 +48,10 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, const Ring& smem, 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float g = acc[i][j][4 * q + e], u = acc[i][j + 2][4 * q + e];
-          z[e] = g / (1.0f + __expf(-g)) * u;
+          // silu(g) = g / (1 + e^-g) with the hardware reciprocal (~1 ulp of
+          // fp32, far below Z's bf16 rounding) instead of an IEEE division
+          // sequence: the epilogue runs with the matrix unit idle
+          z[e] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
         }
         St::put(reg, i * 32 + lr, j * 32 + acc_col(q, lh), pack_bf16x2(z[0], z[1]),
                 pack_bf16x2(z[2], z[3]));

@@ -95,7 +95,7 @@ __device__ __forceinline__ void bwd_gu_tile(const FfnArgs& a, const Ring& smem, 
           const unsigned bits = e & 1 ? (dzv[e >> 1] & 0xFFFF0000u) : (dzv[e >> 1] << 16);
           const float dz = __uint_as_float(bits);
           const float g = acc[i][j][4 * q + e], u = acc[i][j + 2][4 * q + e];
-          const float sg = 1.0f / (1.0f + __expf(-g));
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));   // as in the forward
           du[e] = dz * (g * sg);
           dg[e] = dz * u * (sg * (1.0f + g * (1.0f - sg)));
         }
