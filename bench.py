@@ -416,6 +416,44 @@ def time_graph(w, buf, batches, home, pool, x, steps):
                     "before each timed step"}
 
 
+def time_per_rank(w, buf, batches, home, pool, x, reps=3):
+    """The grouped FFN of each virtual rank on its own (moonep_expert_ffn with
+    rank = d) at the first and the last routing of the sweep: the slowest and
+    the mean rank, per rank 6 S K H H' flop.  The balanced plan gives every
+    rank exactly S K slots, so the ranks stay level however skewed the
+    routing."""
+    import torch
+    dev = x.device
+    plan = buf.new_plan()
+    x_nvs = torch.empty((w.R, buf.NvS, w.H), dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x_nvs)
+    z = torch.empty((w.R, buf.NvS, w.Hp), dtype=torch.bfloat16, device=dev)
+    flops = 6.0 * w.S * w.K * w.H * w.Hp
+    out = {}
+    for t, topk, rw in (batches[0], batches[-1]):
+        buf.plan(topk, plan=plan)
+        buf.dispatch(plan, x, rw, x_nvs=x_nvs)
+        buf.prefetch_weight(plan, home, pool)
+        ms = []
+        for d in range(w.R):
+            buf.expert_ffn(plan, x_nvs, home, pool, z_ws=z, y_nvs=y, rank=d)   # warm
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            for _ in range(reps):
+                buf.expert_ffn(plan, x_nvs, home, pool, z_ws=z, y_nvs=y, rank=d)
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms.append(ev[0].elapsed_time(ev[1]) / reps)
+        out[str(t)] = {"rank_ms": [round(v, 3) for v in ms], "slowest_ms": round(max(ms), 3),
+                       "mean_ms": round(float(np.mean(ms)), 3),
+                       "slowest_TFLOPs": round(flops / (max(ms) * 1e-3) / 1e12, 1),
+                       "mean_TFLOPs": round(flops / (float(np.mean(ms)) * 1e-3) / 1e12, 1),
+                       "slowest_over_mean": round(max(ms) / float(np.mean(ms)), 3)}
+    out["note"] = ("each rank's FFN launched on its own (one rank's tiles fill the GPU less "
+                   "than the all-rank launch timed above); slowest_over_mean is the balance")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -579,6 +617,8 @@ def main():
         for k in keys:
             sweep[k]["ffn_over_first"] = round(sweep[k]["ffn_ms"] / sweep[t0]["ffn_ms"], 3)
             sweep[k]["pdc_over_first"] = round(sweep[t0]["pdc_GBps"] / sweep[k]["pdc_GBps"], 3)
+            for st in ("plan_us", "dispatch_us", "combine_us"):
+                sweep[k][st.split("_")[0] + "_over_first"] = round(sweep[k][st] / sweep[t0][st], 3)
 
     # algorithmic FFN bytes averaged over the timed steps (each step's plan)
     gu_bytes = float(np.mean([stats[u]["gateup_bytes"] for u in used]))
@@ -611,6 +651,12 @@ def main():
                              "traffic": None, "per_launch": {"bytes": cb, "avg_s": t_comb}},
         "sweep": sweep,
     }
+    result["per_rank_ffn"] = time_per_rank(w, buf, batches, home, pool, x)
+    props = torch.cuda.get_device_properties(0)
+    result["device"] = {"name": getattr(props, "name", None),
+                        "arch": getattr(props, "gcnArchName", None),
+                        "compute_units": getattr(props, "multi_processor_count", None)}
+
     # the copy that zero-copy avoids (README "API guide > zero_copy"): copy
     # mode adds one copy of the used slots to dispatch and one to combine
     t_last, topk_last, _ = batches[-1]
