@@ -528,15 +528,34 @@ __device__ __forceinline__ const uint16_t* weight_row(const FfnArgs& a, int p, i
 // group start * 16 + group size); the workgroups of a group starting at tile
 // g with size n are those with index l in [g ntn, (g + n) ntn), so l / ntn is
 // a tile of the same group and names it.
+//
+// The workgroups enumerate only real tiles: the launched ranks' tiles, rank
+// after rank, each N-swept as above, and XCD x takes the x-th eighth of that
+// list.  (Splitting the grid's padded range instead gives the empty tail of
+// each rank's upper bound to whole XCDs: one rank launched alone would keep
+// only five of the eight busy.)  The rank counts are read with uniform
+// loads, which the scalar cache serves: a per-lane load and scan here
+// measurably delayed every workgroup's start.
 __device__ __forceinline__ bool decode(const FfnArgs& a, int* d, Tile* tl, int* nt) {
-  const int64_t lt = logical_tile();
-  const int64_t per_rank = (int64_t)a.max_tiles * a.ntn;
-  const int64_t total = (int64_t)a.nranks * per_rank;
+  int64_t total = 0;
+  for (int i = 0; i < a.nranks; ++i) total += a.ntiles[a.rank0 + i];
+  total *= a.ntn;
+  const int64_t per_xcd = (total + kXcds - 1) / kXcds;
+  const int64_t b = blockIdx.x;
+  const int64_t c = b / kXcds;
+  if (c >= per_xcd) return false;
+  const int64_t lt = (b % kXcds) * per_xcd + c;
   if (lt >= total) return false;
-  *d = a.rank0 + (int)(lt / per_rank);
-  const int l = (int)(lt % per_rank);
+  int r = 0;
+  int64_t first = 0;                                   // tiles of the ranks before r
+  for (; r < a.nranks - 1; ++r) {                      // lt < total: the last rank ends it
+    const int n = a.ntiles[a.rank0 + r];
+    if ((first + n) * a.ntn > lt) break;
+    first += n;
+  }
+  *d = a.rank0 + r;
+  const int l = (int)(lt - (int64_t)first * a.ntn);
   const int tp = l / a.ntn;
-  if (tp >= a.ntiles[*d]) return false;
   const int32_t* base = a.tiles + (int64_t)*d * a.max_tiles * 4;
   const int grp = base[tp * 4 + 3];
   const int gs = grp >> 4, gm = grp & 15;
