@@ -472,6 +472,9 @@ def main():
     ap.add_argument("--overlap", action="store_true",
                     help="also time two pipelined micro-batches with dispatch/combine on a "
                          "second stream at a 32-CU budget against running them back to back")
+    ap.add_argument("--no-per-rank", action="store_true",
+                    help="skip the per-virtual-rank FFN leg (profiling runs: keeps the kernel "
+                         "statistics to the timed steps' launches)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the forward step as one HIP graph replayed for every "
                          "routing beside the same step launched eagerly")
@@ -651,7 +654,8 @@ def main():
                              "traffic": None, "per_launch": {"bytes": cb, "avg_s": t_comb}},
         "sweep": sweep,
     }
-    result["per_rank_ffn"] = time_per_rank(w, buf, batches, home, pool, x)
+    if not args.no_per_rank:
+        result["per_rank_ffn"] = time_per_rank(w, buf, batches, home, pool, x)
     props = torch.cuda.get_device_properties(0)
     result["device"] = {"name": getattr(props, "name", None),
                         "arch": getattr(props, "gcnArchName", None),

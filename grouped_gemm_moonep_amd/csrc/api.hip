@@ -48,7 +48,8 @@ bool dims_from_config(const moonep_config_t* cfg, Dims* out) {
   d.max_tiles = (int)(ceil_div(d.NvS, kGemmTileM) + 2 * d.L);
   a.tiles = a.hold + RB;
   a.ntiles = a.tiles + 4LL * c.R * d.max_tiles;
-  a.total = a.ntiles + c.R;
+  a.nfull = a.ntiles + c.R;
+  a.total = a.nfull + c.R;
   *out = d;
   return true;
 }

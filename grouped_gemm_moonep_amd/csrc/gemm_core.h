@@ -510,6 +510,7 @@ struct FfnArgs {
   uint16_t* dx;
   const int32_t* tiles;     // [R][max_tiles][4]
   const int32_t* ntiles;    // [R]
+  const int32_t* nfull;     // [R] full-duration tiles of each rank (the first ones)
   int R, E, B, H, Hp, NvS, max_tiles, rank0, nranks, ntn;
 };
 
@@ -529,31 +530,43 @@ __device__ __forceinline__ const uint16_t* weight_row(const FfnArgs& a, int p, i
 // g with size n are those with index l in [g ntn, (g + n) ntn), so l / ntn is
 // a tile of the same group and names it.
 //
-// The workgroups enumerate only real tiles: the launched ranks' tiles, rank
-// after rank, each N-swept as above, and XCD x takes the x-th eighth of that
-// list.  (Splitting the grid's padded range instead gives the empty tail of
-// each rank's upper bound to whole XCDs: one rank launched alone would keep
-// only five of the eight busy.)  The rank counts are read with uniform
-// loads, which the scalar cache serves: a per-lane load and scan here
-// measurably delayed every workgroup's start.
+// The workgroups enumerate only real tiles, in two parts: every launched
+// rank's full-duration tiles (rank after rank, each N-swept as above), then
+// every rank's short tiles; XCD x takes the x-th contiguous eighth of that
+// list.  Each part keeps tiles of one duration together whatever the ranks'
+// tile counts, so the tiles an XCD runs together stay in step; splitting the
+// grid's padded upper bound instead would give the empty tail of each rank's
+// range to whole XCDs (one rank launched alone kept only five of the eight
+// busy).  The rank counts are read with uniform loads, which the scalar cache
+// serves (a per-lane load and scan measurably delayed every workgroup's
+// start).
 __device__ __forceinline__ bool decode(const FfnArgs& a, int* d, Tile* tl, int* nt) {
-  int64_t total = 0;
-  for (int i = 0; i < a.nranks; ++i) total += a.ntiles[a.rank0 + i];
-  total *= a.ntn;
+  int64_t nf = 0, ns = 0;
+  for (int i = 0; i < a.nranks; ++i) {
+    const int f = a.nfull[a.rank0 + i];
+    nf += f;
+    ns += a.ntiles[a.rank0 + i] - f;
+  }
+  const int64_t total = (nf + ns) * a.ntn;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const int64_t b = blockIdx.x;
   const int64_t c = b / kXcds;
   if (c >= per_xcd) return false;
-  const int64_t lt = (b % kXcds) * per_xcd + c;
+  int64_t lt = (b % kXcds) * per_xcd + c;
   if (lt >= total) return false;
+  const bool full = lt < nf * a.ntn;
+  if (!full) lt -= nf * a.ntn;
+  // the rank: count of this part's tiles in the ranks before it
   int r = 0;
-  int64_t first = 0;                                   // tiles of the ranks before r
-  for (; r < a.nranks - 1; ++r) {                      // lt < total: the last rank ends it
-    const int n = a.ntiles[a.rank0 + r];
+  int64_t first = 0;
+  for (; r < a.nranks - 1; ++r) {                      // lt lies in the part: the last rank ends it
+    const int f = a.nfull[a.rank0 + r];
+    const int n = full ? f : a.ntiles[a.rank0 + r] - f;
     if ((first + n) * a.ntn > lt) break;
     first += n;
   }
   *d = a.rank0 + r;
+  if (!full) lt += (int64_t)a.nfull[*d] * a.ntn;       // the rank's short tiles follow its full ones
   const int l = (int)(lt - (int64_t)first * a.ntn);
   const int tp = l / a.ntn;
   const int32_t* base = a.tiles + (int64_t)*d * a.max_tiles * 4;
@@ -597,7 +610,7 @@ static inline FfnArgs ffn_args(const Ctx& c, const moonep_plan_t& p, int rank,
   a.pstride = w.pool_stride;
   a.x = nullptr; a.z = nullptr; a.zin = nullptr; a.y = nullptr;
   a.dy = nullptr; a.dz = nullptr; a.dg = nullptr; a.du = nullptr; a.dx = nullptr;
-  a.tiles = p.aux + d.aux.tiles; a.ntiles = p.aux + d.aux.ntiles;
+  a.tiles = p.aux + d.aux.tiles; a.ntiles = p.aux + d.aux.ntiles; a.nfull = p.aux + d.aux.nfull;
   a.R = d.R; a.E = d.E; a.B = d.B; a.H = d.H; a.Hp = d.Hp; a.NvS = (int)d.NvS;
   a.max_tiles = d.max_tiles;
   a.rank0 = rank < 0 ? 0 : rank;

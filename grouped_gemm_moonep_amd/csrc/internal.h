@@ -27,6 +27,7 @@ struct AuxLayout {
   int64_t hold;     // [R*B] holder slots d*B+j grouped by expert, ascending d
   int64_t tiles;    // [R][max_tiles][4] grouped-GEMM M-tiles (row, first slot, end slot, 0)
   int64_t ntiles;   // [R] M-tiles of each rank
+  int64_t nfull;    // [R] of which full-duration (they come first)
   int64_t total;
 };
 

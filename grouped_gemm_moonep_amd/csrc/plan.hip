@@ -537,7 +537,8 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
     // built from plan_solve's segments alongside the token assignment
     __shared__ int wsum[4];
     build_tile_schedule(a.aux + a.ax.act, a.cu, a.segn, a.aux + a.ax.tiles,
-                        a.aux + a.ax.ntiles, blockIdx.y, 2 * a.L, a.E + a.B, a.tp, a.max_tiles,
+                        a.aux + a.ax.ntiles, a.aux + a.ax.nfull, blockIdx.y, 2 * a.L,
+                        a.E + a.B, a.tp, a.max_tiles,
                         wsum);
     return;
   }

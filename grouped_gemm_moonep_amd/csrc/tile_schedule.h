@@ -47,7 +47,8 @@ __device__ __forceinline__ int block_scan256(int v, int* total, int (&wsum)[4]) 
 
 __device__ __forceinline__ void build_tile_schedule(const int32_t* act, const int32_t* cu,
                                                     const int32_t* segn, int32_t* tiles,
-                                                    int32_t* ntiles, int d, int L2, int EB,
+                                                    int32_t* ntiles, int32_t* nfull, int d,
+                                                    int L2, int EB,
                                                     int tp, int max_tiles, int (&wsum)[4]) {
   const int tid = threadIdx.x;
   int32_t* rank_tiles = tiles + (int64_t)d * max_tiles * 4;
@@ -104,6 +105,7 @@ __device__ __forceinline__ void build_tile_schedule(const int32_t* act, const in
   if (tid == 0) {
     const int n = nfull_all + nshort_all;
     ntiles[d] = n < max_tiles ? n : max_tiles;
+    nfull[d] = nfull_all < max_tiles ? nfull_all : max_tiles;
   }
 }
 
