@@ -107,7 +107,7 @@ hipError_t launch_gateup(const Ctx& c, const moonep_plan_t& p, int rank, const u
   a.x = x_nvs;
   a.z = z;
   a.ntn = (c.d.Hp + 127) / 128;
-  ffn_gateup<<<(unsigned)pad_grid((int64_t)a.nranks * a.max_tiles * a.ntn), kThreads, 0, s>>>(a);
+  ffn_gateup<<<(unsigned)tile_grid(a), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -117,7 +117,7 @@ hipError_t launch_down(const Ctx& c, const moonep_plan_t& p, int rank, const uin
   a.zin = z;
   a.y = y;
   a.ntn = (c.d.H + BN - 1) / BN;
-  ffn_down<<<(unsigned)pad_grid((int64_t)a.nranks * a.max_tiles * a.ntn), kThreads, 0, s>>>(a);
+  ffn_down<<<(unsigned)tile_grid(a), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

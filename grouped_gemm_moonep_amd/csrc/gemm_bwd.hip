@@ -232,13 +232,12 @@ hipError_t launch_ffn_bwd(const Ctx& c, const moonep_plan_t& p, int rank, const 
                           uint16_t* du, uint16_t* dx, hipStream_t s) {
   FfnArgs a = ffn_args(c, p, rank, w);
   a.x = x; a.dy = dy; a.dz = dz; a.dg = dg; a.du = du; a.dx = dx;
-  const int64_t slots = (int64_t)a.nranks * a.max_tiles;
   a.ntn = (c.d.Hp + BN - 1) / BN;
-  ffn_bwd_dz<<<(unsigned)pad_grid(slots * a.ntn), kThreads, 0, s>>>(a);
+  ffn_bwd_dz<<<(unsigned)tile_grid(a), kThreads, 0, s>>>(a);
   a.ntn = (c.d.Hp + 127) / 128;
-  ffn_bwd_gu<<<(unsigned)pad_grid(slots * a.ntn), kThreads, 0, s>>>(a);
+  ffn_bwd_gu<<<(unsigned)tile_grid(a), kThreads, 0, s>>>(a);
   a.ntn = (c.d.H + BN - 1) / BN;
-  ffn_bwd_dx<<<(unsigned)pad_grid(slots * a.ntn), kThreads, 0, s>>>(a);
+  ffn_bwd_dx<<<(unsigned)tile_grid(a), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

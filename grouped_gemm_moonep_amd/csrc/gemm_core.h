@@ -532,14 +532,14 @@ __device__ __forceinline__ const uint16_t* weight_row(const FfnArgs& a, int p, i
 //
 // The workgroups enumerate only real tiles, in two parts: every launched
 // rank's full-duration tiles (rank after rank, each N-swept as above), then
-// every rank's short tiles; XCD x takes the x-th contiguous eighth of that
-// list.  Each part keeps tiles of one duration together whatever the ranks'
-// tile counts, so the tiles an XCD runs together stay in step; splitting the
-// grid's padded upper bound instead would give the empty tail of each rank's
-// range to whole XCDs (one rank launched alone kept only five of the eight
-// busy).  The rank counts are read with uniform loads, which the scalar cache
-// serves (a per-lane load and scan measurably delayed every workgroup's
-// start).
+// every rank's short tiles.  XCD x runs the x-th eighth of the first part,
+// then the x-th eighth of the second, so every XCD holds the same mix of
+// durations and finishes with the others, and the tiles an XCD runs together
+// have one duration whatever the ranks' tile counts.  Splitting the grid's
+// padded upper bound instead would give the empty tail of each rank's range
+// to whole XCDs (one rank launched alone kept only five of the eight busy).
+// The rank counts are read with uniform loads, which the scalar cache serves
+// (a per-lane load and scan measurably delayed every workgroup's start).
 __device__ __forceinline__ bool decode(const FfnArgs& a, int* d, Tile* tl, int* nt) {
   int64_t nf = 0, ns = 0;
   for (int i = 0; i < a.nranks; ++i) {
@@ -547,15 +547,19 @@ __device__ __forceinline__ bool decode(const FfnArgs& a, int* d, Tile* tl, int* 
     nf += f;
     ns += a.ntiles[a.rank0 + i] - f;
   }
-  const int64_t total = (nf + ns) * a.ntn;
-  const int64_t per_xcd = (total + kXcds - 1) / kXcds;
-  const int64_t b = blockIdx.x;
-  const int64_t c = b / kXcds;
-  if (c >= per_xcd) return false;
-  int64_t lt = (b % kXcds) * per_xcd + c;
-  if (lt >= total) return false;
-  const bool full = lt < nf * a.ntn;
-  if (!full) lt -= nf * a.ntn;
+  const int64_t F = nf * a.ntn, Sx = ns * a.ntn;        // full and short workgroups
+  const int64_t pf = (F + kXcds - 1) / kXcds, ps = (Sx + kXcds - 1) / kXcds;
+  const int64_t x = blockIdx.x % kXcds, c = blockIdx.x / kXcds;
+  const int64_t f0 = x * pf;
+  const int64_t nfx = f0 < F ? (F - f0 < pf ? F - f0 : pf) : 0;   // this XCD's full ones
+  const bool full = c < nfx;
+  int64_t lt;
+  if (full) {
+    lt = f0 + c;
+  } else {
+    lt = x * ps + (c - nfx);
+    if (c - nfx >= ps || lt >= Sx) return false;
+  }
   // the rank: count of this part's tiles in the ranks before it
   int r = 0;
   int64_t first = 0;
@@ -617,6 +621,13 @@ static inline FfnArgs ffn_args(const Ctx& c, const moonep_plan_t& p, int rank,
   a.nranks = rank < 0 ? d.R : 1;
   a.ntn = 0;
   return a;
+}
+
+// Workgroups a tile launch needs: at most max_tiles tiles per launched rank,
+// each swept over ntn N-tiles; rounding each part up per XCD adds at most two
+// workgroups to each XCD.
+static inline int64_t tile_grid(const FfnArgs& a) {
+  return pad_grid((int64_t)a.nranks * a.max_tiles * a.ntn) + 2 * kXcds;
 }
 
 }  // namespace moonep
