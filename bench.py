@@ -171,6 +171,8 @@ def time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool, steps, warmup)
     rbuf = [torch.zeros((w.R, w.B, w.H, w.Hp), dtype=torch.float32, device=dev) for _ in range(3)]
     names = ["combine_bwd", "ffn_bwd", "dispatch_bwd", "wgrad_x3", "reduce_grad"]
     per = {n: [] for n in names}
+    wgrad_bytes = []
+    EB = w.E + w.B
     for i in range(warmup + steps):
         _, topk, _ = batches[i % len(batches)]
         buf.plan(topk, plan=plan)
@@ -195,19 +197,20 @@ def time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool, steps, warmup)
         if i >= warmup:
             for j, n in enumerate(names):
                 per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
+            # each used (rank, weight row) pair's fp32 gradient rows are read and
+            # written once per projection; each segment row of the two operands
+            # of each product is read once
+            seg = plan.arrays["seg_tokens"].cpu().numpy().reshape(w.R, EB)
+            rows = int(plan.arrays["cu_seqlens"].cpu().numpy().reshape(w.R, EB)[:, -1].sum())
+            wgrad_bytes.append(3 * int((seg > 0).sum()) * float(w.H) * w.Hp * 4 * 2
+                               + 3 * rows * (w.H + w.Hp) * 2)
     slots = w.R * w.S * w.K
     hh = float(w.H) * w.Hp
     mean = {n: float(np.mean(v)) for n, v in per.items()}
     out = {n + "_ms": round(t * 1e3, 3) for n, t in mean.items()}
     out["ffn_bwd_TFLOPs"] = round(10 * hh * slots / mean["ffn_bwd"] / 1e12, 1)
     out["wgrad_TFLOPs"] = round(6 * hh * slots / mean["wgrad_x3"] / 1e12, 1)
-    # weight gradients are HBM-bound: every gradient row (E home + R*B reduce
-    # slots, fp32) is read and written once per projection (accumulation),
-    # plus the bf16 operands of the three products
-    nvs_rows = w.R * buf.NvS
-    wgrad_bytes = 3 * (w.E + w.R * w.B) * hh * 4 * 2 + 2 * nvs_rows * (2 * w.H + 2 * w.Hp) \
-        + nvs_rows * (2 * w.H + 2 * w.Hp)
-    out["wgrad_GBps"] = round(wgrad_bytes / mean["wgrad_x3"] / 1e9, 1)
+    out["wgrad_GBps"] = round(sum(wgrad_bytes) / sum(per["wgrad_x3"]) / 1e9, 1)
     pb, db, cb = alg_bytes(w)
     out["combine_bwd_GBps"] = round(db / mean["combine_bwd"] / 1e9, 1)
     out["dispatch_bwd_GBps"] = round((slots * 2 * w.H + w.R * w.S * 2 * w.H + 4 * slots)
@@ -215,8 +218,8 @@ def time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool, steps, warmup)
     out["backward_ms"] = round(sum(mean.values()) * 1e3, 3)
     out["note"] = ("flops per real slot: FFN backward 10 H H' (dZ 2, recomputed gate/up 4, "
                    "dX 4), weight gradients 6 H H'; weight-gradient bytes: fp32 read-modify-"
-                   "write of every gradient row per projection plus the bf16 operands; steps "
-                   "cycle the same maxvio targets")
+                   "write of each used (rank, weight row) pair's gradient per projection plus "
+                   "the bf16 operand rows once; steps cycle the same maxvio targets")
     return out
 
 

@@ -79,6 +79,8 @@ __device__ __forceinline__ void bwd_gu_tile(const FfnArgs& a, const Ring& smem, 
   lds_t* reg_u = reg_g + St::kBytes;
   const uint16_t* dzb = a.dz + ((int64_t)d * a.NvS + tl.m0) * a.Hp + n0;
   typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  // every dZ read of the tile is issued before the first is used
+  u32x2 dzv[MI][2][4];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -87,12 +89,20 @@ __device__ __forceinline__ void bwd_gu_tile(const FfnArgs& a, const Ring& smem, 
       for (int q = 0; q < 4; ++q) {
         const int m = wm * 32 * MI + i * 32 + lr;
         const int n = wn * 64 + j * 32 + acc_col(q, lh);
-        u32x2 dzv = {0u, 0u};
-        if (m < rows_valid && n < nvh) dzv = *(const u32x2*)(dzb + (int64_t)m * a.Hp + n);
+        dzv[i][j][q] = u32x2{0u, 0u};
+        if (m < rows_valid && n < nvh) dzv[i][j][q] = *(const u32x2*)(dzb + (int64_t)m * a.Hp + n);
+      }
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
         float dg[4], du[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const unsigned bits = e & 1 ? (dzv[e >> 1] & 0xFFFF0000u) : (dzv[e >> 1] << 16);
+          const unsigned w = dzv[i][j][q][e >> 1];
+          const unsigned bits = e & 1 ? (w & 0xFFFF0000u) : (w << 16);
           const float dz = __uint_as_float(bits);
           const float g = acc[i][j][4 * q + e], u = acc[i][j + 2][4 * q + e];
           const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));   // as in the forward
@@ -205,24 +215,35 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   const int64_t rs = (int64_t)a.H * a.Hp;
   float* G = (row < a.E ? a.gh + (int64_t)row * rs : a.rb + ((int64_t)d * a.B + row - a.E) * rs) +
              (int64_t)m0 * a.Hp + n0;
+  // The 16 reads of a row block are issued together before any write: a
+  // read after a write the compiler cannot prove disjoint would otherwise
+  // wait for each read in turn.
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
   typedef float f32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int m = wm * 128 + i * 32 + lr;
+    float* grow = G + (int64_t)m * a.Hp;
+    f32x4 v[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int m = wm * 128 + i * 32 + lr;
+        const int n = nrow[j] + acc_col(q, lh);
+        if (m < mv && n < nv) v[j][q] = *(const f32x4*)(grow + n);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
         const int n = nrow[j] + acc_col(q, lh);
         if (m < mv && n < nv) {
-          f32x4* gp = (f32x4*)(G + (int64_t)m * a.Hp + n);
-          f32x4 v = *gp;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = __fadd_rn(v[e], acc[i][j][4 * q + e]);
-          *gp = v;
+          for (int e = 0; e < 4; ++e) v[j][q][e] = __fadd_rn(v[j][q][e], acc[i][j][4 * q + e]);
+          *(f32x4*)(grow + n) = v[j][q];
         }
       }
+  }
 }
 
 }  // namespace
