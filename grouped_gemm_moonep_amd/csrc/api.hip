@@ -49,7 +49,8 @@ bool dims_from_config(const moonep_config_t* cfg, Dims* out) {
   a.tiles = a.hold + RB;
   a.ntiles = a.tiles + 4LL * c.R * d.max_tiles;
   a.nfull = a.ntiles + c.R;
-  a.total = a.nfull + c.R;
+  a.nact = a.nfull + c.R;
+  a.total = a.nact + c.R;
   *out = d;
   return true;
 }

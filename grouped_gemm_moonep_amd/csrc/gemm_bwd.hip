@@ -170,24 +170,44 @@ struct WgradArgs {
   float* gh;                // [E][H][Hp]
   float* rb;                // [R*B][H][Hp]
   const int32_t* act;       // [R][2L]
+  const int32_t* nact;      // [R] active rows (the first entries of act)
   const int32_t* cu;        // [R][E+B]
   const int32_t* segn;      // [R][E+B]
   int R, E, B, H, Hp, NvS, L2, EB, tp, rank0, nranks, ntm, ntn;
 };
+
+constexpr int kWgradChunk = 32;   // CUs per XCD
 
 // dW[h][h'] += sum over the segment's tokens t of A[t][h] * B[t][h'].
 // Tile: 256 h (MFMA rows) x 256 h' (MFMA columns), contraction over t.
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1))) void wgrad_kernel(WgradArgs a) {
   MOONEP_RING(smem);
-  const int64_t lt = logical_tile();
-  const int64_t total = (int64_t)a.nranks * a.L2 * a.ntm * a.ntn;
+  // Only real tiles are enumerated: the launched ranks' active rows, rank
+  // after rank, each swept over its ntm x ntn output tiles (N fastest).  The
+  // list is cut into chunks of 32 tiles, one wave of an XCD's CUs, and XCD x
+  // takes chunks x, x + 8, x + 16, ...: each XCD gets a like share of every
+  // segment, whose tiles last in proportion to its token count, so the XCDs
+  // end together whether one rank or all are launched.  (Contiguous eighths
+  // of the grid's padded bound gave whole XCDs only the empty tiles of unused
+  // slots when one rank is launched alone; contiguous eighths of the real
+  // tiles gave them unequal token counts.)  Uniform loads: the scalar cache
+  // serves them.
+  const int64_t per_row = (int64_t)a.ntm * a.ntn;
+  int64_t nrows = 0;
+  for (int i = 0; i < a.nranks; ++i) nrows += a.nact[a.rank0 + i];
+  const int64_t total = nrows * per_row;
+  const int64_t c = blockIdx.x / kXcds;
+  const int64_t lt = ((c / kWgradChunk) * kXcds + blockIdx.x % kXcds) * kWgradChunk +
+                     c % kWgradChunk;
   if (lt >= total) return;
-  const int tn = (int)(lt % a.ntn);
-  const int tm = (int)((lt / a.ntn) % a.ntm);
-  const int q = (int)((lt / ((int64_t)a.ntn * a.ntm)) % a.L2);
-  const int d = a.rank0 + (int)(lt / ((int64_t)a.ntn * a.ntm * a.L2));
-  const int row = a.act[d * a.L2 + q];
+  int64_t qi = lt / per_row;                           // active row across the launched ranks
+  int d = a.rank0;
+  for (; d < a.rank0 + a.nranks - 1 && qi >= a.nact[d]; ++d) qi -= a.nact[d];
+  const int64_t rem = lt % per_row;
+  const int tn = (int)(rem % a.ntn);
+  const int tm = (int)(rem / a.ntn);
+  const int row = a.act[d * a.L2 + (int)qi];
   if (row < 0) return;
   const int end = a.cu[d * a.EB + row];
   const int ntok = a.segn[d * a.EB + row];
@@ -267,7 +287,8 @@ hipError_t launch_wgrad(const Ctx& c, const moonep_plan_t& p, int rank, const ui
   const Dims& d = c.d;
   WgradArgs a;
   a.a = A; a.b = B; a.gh = gh; a.rb = rb;
-  a.act = p.aux + d.aux.act; a.cu = p.cu_seqlens; a.segn = p.seg_tokens;
+  a.act = p.aux + d.aux.act; a.nact = p.aux + d.aux.nact;
+  a.cu = p.cu_seqlens; a.segn = p.seg_tokens;
   a.R = d.R; a.E = d.E; a.B = d.B; a.H = d.H; a.Hp = d.Hp; a.NvS = (int)d.NvS;
   a.L2 = 2 * d.L; a.EB = d.E + d.B; a.tp = d.tp;
   a.rank0 = rank < 0 ? 0 : rank;
@@ -275,7 +296,8 @@ hipError_t launch_wgrad(const Ctx& c, const moonep_plan_t& p, int rank, const ui
   a.ntm = (d.H + BM - 1) / BM;
   a.ntn = (d.Hp + BN - 1) / BN;
   const int64_t total = (int64_t)a.nranks * a.L2 * a.ntm * a.ntn;
-  wgrad_kernel<<<(unsigned)pad_grid(total), kThreads, 0, s>>>(a);
+  const int64_t chunks = kXcds * kWgradChunk;   // the grid covers whole rounds of chunks
+  wgrad_kernel<<<(unsigned)((total + chunks - 1) / chunks * chunks), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

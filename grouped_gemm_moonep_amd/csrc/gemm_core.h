@@ -482,14 +482,6 @@ struct Stage {
   }
 };
 
-// XCD-aware tile id: XCD x (= block id mod 8) walks the x-th contiguous
-// eighth of the logical tile range.
-__device__ __forceinline__ int64_t logical_tile() {
-  const int64_t g = gridDim.x;                  // a multiple of kXcds
-  const int64_t b = blockIdx.x;
-  return (b % kXcds) * (g / kXcds) + b / kXcds;
-}
-
 struct Tile {
   int row, m0, m1;
 };

@@ -28,6 +28,7 @@ struct AuxLayout {
   int64_t tiles;    // [R][max_tiles][4] grouped-GEMM M-tiles (row, first slot, end slot, 0)
   int64_t ntiles;   // [R] M-tiles of each rank
   int64_t nfull;    // [R] of which full-duration (they come first)
+  int64_t nact;     // [R] active rows of each rank (the first entries of act)
   int64_t total;
 };
 

@@ -436,6 +436,7 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   for (int d = tid; d < R; d += kSolveThreads) {
     const int next = d + 1 < R ? ord_cnt[(d + 1) * S3] : tot_cnt;
     nact[d] = next - ord_cnt[d * S3];
+    a.aux[a.ax.nact + d] = nact[d];
     const int rem = nrem[d];
     a.stats[MOONEP_STAT_REMOTE_GROUP + d] = rem ? recv_g[d] : -1;
     a.stats[MOONEP_STAT_REMOTE_GROUP + R + d] = rem;

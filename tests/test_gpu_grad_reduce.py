@@ -93,6 +93,34 @@ def test_grads_equal_dense_expert_grads(name, target):
     buf.destroy()
 
 
+@pytest.mark.parametrize("name,target", [("tiny_r4_s64_k2_e8", 1.0),
+                                         ("bwd_r8_s1024_k4_e32", 2.0)])
+def test_wgrad_per_rank_launches_equal_one_launch(name, target):
+    """Each rank's weight gradients launched alone (rank = d, as with one GPU
+    per rank) give, bit for bit, what one launch over all ranks gives: every
+    output tile is computed the same way whichever launch enumerates it."""
+    w = synth.WORKLOADS[name]
+    log(f"wgrad per rank {name} target={target}")
+    topk, _ = synth.routing(w, target)
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    x_nvs, _ = buf.dispatch(plan, dev_bf16(synth.hidden(w)))
+    dy_nvs, _ = buf.dispatch(plan, dev_bf16(synth.grad_out(w, w.Hp)))
+    rng = np.random.default_rng(5)
+    gh0 = dev(rng.standard_normal((w.E, w.H, w.Hp), dtype=np.float32))
+    rb0 = dev(rng.standard_normal((w.R, w.B, w.H, w.Hp), dtype=np.float32))
+    gh_all, rb_all = gh0.clone(), rb0.clone()
+    buf.expert_wgrad(plan, x_nvs, dy_nvs, gh_all, rb_all)
+    gh_one, rb_one = gh0.clone(), rb0.clone()
+    for d in range(w.R):
+        buf.expert_wgrad(plan, x_nvs, dy_nvs, gh_one, rb_one, rank=d)
+    torch.cuda.synchronize()
+    assert not torch.equal(gh_all, gh0)
+    assert torch.equal(gh_one, gh_all)
+    assert torch.equal(rb_one, rb_all)
+    buf.destroy()
+
+
 def test_backward_data_path():
     """dispatch bwd (unweighted combine of a width-H gradient) against the
     oracle, bit for bit."""
