@@ -101,7 +101,6 @@ hipError_t launch_wgrad(const Ctx& c, const moonep_plan_t& p, int rank,
 
 // M-tile of the grouped GEMMs (rows of one segment handled by a workgroup).
 constexpr int kGemmTileM = 256;
-constexpr int kWgradTileM = 64;   // tokens per k-step of the weight gradient
 
 }  // namespace moonep
 
