@@ -13,7 +13,7 @@ import torch
 
 import moonep_synth as synth
 import oracle
-from gpu_util import buffer_for, dev, dev_bf16, log, rel_l2
+from gpu_util import buffer_for, dev, dev_bf16, host_bf16, log, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -118,6 +118,46 @@ def test_wgrad_per_rank_launches_equal_one_launch(name, target):
     assert not torch.equal(gh_all, gh0)
     assert torch.equal(gh_one, gh_all)
     assert torch.equal(rb_one, rb_all)
+    buf.destroy()
+
+
+def test_wgrad_full_size_sampled():
+    """Headline shapes, all ranks in one launch, into zeroed gradient rows.
+    A weight gradient separates over its output columns, so the oracle runs
+    the whole plan on sampled columns of both operands (its own dispatch of
+    the same inputs, restricted to those columns) and every home row and
+    used slot is compared on those columns."""
+    w = synth.WORKLOADS["fwd_r8_s4096_k8_e256"]
+    log("wgrad full size")
+    topk, _ = synth.routing(w, 2.0)
+    p = oracle.plan(topk, w.E, w.B, w.token_padding)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn((w.R, w.S, w.H), generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn((w.R, w.S, w.Hp), generator=g, device="cuda").to(torch.bfloat16)
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    x_nvs, _ = buf.dispatch(plan, x)
+    b_nvs, _ = buf.dispatch(plan, b)
+    gh = torch.zeros((w.E, w.H, w.Hp), device="cuda")
+    rb = torch.zeros((w.R, w.B, w.H, w.Hp), device="cuda")
+    buf.expert_wgrad(plan, x_nvs, b_nvs, gh, rb)
+    torch.cuda.synchronize()
+    del x_nvs, b_nvs
+    rng = np.random.default_rng(12)
+    hs = np.unique(np.concatenate([[0, w.H - 1], rng.choice(w.H, 46, replace=False)]))
+    hps = np.unique(np.concatenate([[0, w.Hp - 1], rng.choice(w.Hp, 46, replace=False)]))
+    hs_d = torch.from_numpy(hs).cuda()
+    hps_d = torch.from_numpy(hps).cuda()
+    got_h = gh.index_select(1, hs_d).index_select(2, hps_d).cpu().numpy()
+    got_r = rb.index_select(2, hs_d).index_select(3, hps_d).cpu().numpy()
+    xa, _ = oracle.dispatch(p, host_bf16(x)[:, :, hs])
+    ba, _ = oracle.dispatch(p, host_bf16(b)[:, :, hps])
+    want_h, want_r = oracle.expert_wgrad(p, xa, ba,
+                                         np.zeros((w.E, len(hs), len(hps)), np.float32),
+                                         np.zeros((w.R, w.B, len(hs), len(hps)), np.float32))
+    assert np.abs(want_h).max() > 1.0 and np.abs(want_r).max() > 1.0
+    assert np.abs(got_h - want_h).max() <= 2e-2 and rel_l2(got_h, want_h) <= 1e-2
+    assert np.abs(got_r - want_r).max() <= 2e-2 and rel_l2(got_r, want_r) <= 1e-2
     buf.destroy()
 
 
