@@ -203,32 +203,41 @@ struct RowTileT {
 typedef RowTileT<8> RowTile;      // 256 rows
 
 // Row tile whose K range is the concatenation of two matrices: k < k1 from
-// the first, k >= k1 from the second (both with the same rows).  koff passes
-// the element index through; each load picks its source (a wave-uniform
-// choice).
+// the first, k >= k1 from the second (same rows, same row stride, so the
+// lane offsets are shared and only the descriptor differs).  koff encodes
+// the step once: the byte offset within the matrix that holds k, with
+// kSecond set for the second; kOob past the end.  Each load then selects a
+// descriptor with scalar selects, with no branch in the MFMA stream (a
+// per-load branch split every step into three copies of its loads).
 template <int NL>
 struct RowTile2 {
   static constexpr bool kRows = true;
   static constexpr int kLoads = NL;
-  RowTileT<NL> t0, t1;
+  static constexpr uint32_t kSecond = 0x40000000u;
+  RowTileT<NL> t;       // geometry and the first matrix's descriptor
+  DmaRsrc rs1;          // the second matrix
   uint32_t k1;
   __device__ __forceinline__ void init(const uint16_t* base0, const uint16_t* base1, int64_t ld,
                                        int rows_valid, int k_first) {
-    t0.init(base0, ld, rows_valid);
-    t1.init(base1, ld, rows_valid);
+    t.init(base0, ld, rows_valid);
+    rs1 = make_dma_rsrc(base1, (int64_t)rows_valid * ld * 2);
     k1 = (uint32_t)k_first;
   }
-  // k: the step's first k, or kOob past the end (both matrices then read zero)
-  __device__ __forceinline__ uint32_t koff(int64_t k0) const { return (uint32_t)k0; }
-  __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t k) const {
-    if (k < k1) t0.issue1(tile, i, t0.koff(k));
-    else if (k == kOob) t1.issue1(tile, i, kOob);
-    else t1.issue1(tile, i, t1.koff(k - k1));
+  __device__ __forceinline__ uint32_t koff(int64_t k0) const {
+    return k0 < k1 ? (uint32_t)(k0 * 2) : ((uint32_t)((k0 - k1) * 2) | kSecond);
+  }
+  __device__ __forceinline__ void issue1(lds_t* tile, int i, uint32_t ko) const {
+    const bool second = (ko & kSecond) != 0;              // never set in kOob
+    const uint32_t s = (ko & ~kSecond) + (uint32_t)i * t.step;
+    DmaRsrc r;                                            // element-wise: scalar selects
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r.v[e] = second ? rs1.v[e] : t.rs.v[e];
+    load_lds(r, tile + t.wlds + i * 1024, t.voff[i & 1] + s);
   }
   __device__ __forceinline__ void issue(lds_t* tile, int64_t k0, bool valid) const {
-    const uint32_t k = valid ? koff(k0) : kOob;
+    const uint32_t ko = valid ? koff(k0) : kOob;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) issue1(tile, i, k);
+    for (int i = 0; i < NL; ++i) issue1(tile, i, ko);
   }
   __device__ __forceinline__ static bf16x8 frag(const lds_t* tile, int row, int kk, int lh) {
     return RowTileT<NL>::frag(tile, row, kk, lh);
