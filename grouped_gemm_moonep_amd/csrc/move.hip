@@ -28,6 +28,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 8;          // 16-byte vectors per lane in flight
+constexpr int kRowVecs = 16;        // 16-byte vectors per lane holding a whole row (W <= 8192)
+constexpr int kDispatchBlocks = 2048;
 
 __device__ __forceinline__ int round_up(int n, int m) { return (n + m - 1) / m * m; }
 
@@ -55,7 +57,10 @@ struct DispatchArgs {
 };
 
 // Blocks [0, npad_blocks): zero the padding rows of one active row (one part
-// of it).  Blocks past that: grid-stride over tokens, one wave per token.
+// of it).  Blocks past that: grid-stride over tokens, one wave per token,
+// which reads the row once and writes it to its K slots: the whole row held
+// in registers when it fits (kWhole), else 8 KiB at a time.
+template <bool kWhole>
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -83,6 +88,22 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs a) {
     const int tok = uniform(t);
     const u32x4* src = a.x + (int64_t)tok * a.nv;
     const int32_t* dk = a.dest + (int64_t)tok * a.K;
+    if constexpr (kWhole) {
+      u32x4 buf[kRowVecs];
+#pragma unroll
+      for (int u = 0; u < kRowVecs; ++u) {
+        const int v = u * 64 + lane;
+        if (v < a.nv) buf[u] = __builtin_nontemporal_load(src + v);
+      }
+      for (int k = 0; k < a.K; ++k) {
+        u32x4* dst = a.x_nvs + (int64_t)uniform(dk[k]) * a.nv;
+#pragma unroll
+        for (int u = 0; u < kRowVecs; ++u) {
+          const int v = u * 64 + lane;
+          if (v < a.nv) dst[v] = buf[u];
+        }
+      }
+    } else
     for (int base = 0; base < a.nv; base += 64 * kUnroll) {
       u32x4 buf[kUnroll];
 #pragma unroll
@@ -298,8 +319,14 @@ hipError_t launch_dispatch(const Ctx& c, const moonep_plan_t& p, const uint16_t*
   a.tp = d.tp; a.NvS = (int)d.NvS;
   a.pad_parts = (d.tp + 4 * kWaves - 1) / (4 * kWaves);
   a.npad_blocks = d.R * a.L2 * a.pad_parts;
-  const int tok_blocks = capped_grid(c, (a.ntok + kWaves * 2 - 1) / (kWaves * 2));
-  dispatch_kernel<<<a.npad_blocks + tok_blocks, kThreads, 0, s>>>(a);
+  if (a.nv <= 64 * kRowVecs) {
+    const int64_t want = (a.ntok + kWaves - 1) / kWaves;
+    const int tok_blocks = capped_grid(c, want < kDispatchBlocks ? want : kDispatchBlocks);
+    dispatch_kernel<true><<<a.npad_blocks + tok_blocks, kThreads, 0, s>>>(a);
+  } else {
+    const int tok_blocks = capped_grid(c, (a.ntok + kWaves * 2 - 1) / (kWaves * 2));
+    dispatch_kernel<false><<<a.npad_blocks + tok_blocks, kThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
