@@ -521,10 +521,10 @@ __device__ __forceinline__ const uint16_t* weight_row(const FfnArgs& a, int p, i
                    : a.pool[p] + ((int64_t)d * a.pstride + row - a.E) * rs;
 }
 
-// Within a rank, tiles are taken in groups of up to kGroupM M-tiles of one
+// Within a rank, tiles are taken in groups of up to kGroupMax M-tiles of one
 // segment (one expert): the group's M-tiles for the first N-tile, then for the
-// second, ...  Workgroups that run together on an XCD (32 CUs) then cover
-// kGroupM M-tiles x 32/kGroupM N-tiles of the same expert, so each weight
+// second, ...  Workgroups that run together on an XCD (32 CUs) then cover a
+// group's n M-tiles x about 32/n N-tiles of the same expert, so each weight
 // slab in that XCD's L2 serves the group's workgroups, and a group never
 // mixes two experts' weights.  Tile entry t holds (row, first slot, end slot,
 // group start * 16 + group size); the workgroups of a group starting at tile

@@ -11,7 +11,7 @@ namespace moonep {
 
 constexpr int kTileM = 256;        // rows of an M-tile
 constexpr int kShortTileM = 128;   // a segment tail of at most this many rows runs as a short tile
-constexpr int kGroupM = 4;         // M-tiles of one segment that share a weight slab in L2
+constexpr int kGroupMax = 8;       // most M-tiles of one segment that share a weight slab in L2
 
 __device__ __forceinline__ int tile_round_up(int n, int m) { return (n + m - 1) / m * m; }
 
@@ -19,9 +19,12 @@ __device__ __forceinline__ int tile_round_up(int n, int m) { return (n + m - 1) 
 // q of the rank).  A segment of padded length len has floor(len/256) tiles of
 // 256 rows; a remainder of more than 128 rows is one more tile of the same
 // duration, and a remainder of at most 128 rows is a short tile (half the
-// rows and half the duration).  Full-duration tiles come first, in segment order, in groups
-// of up to kGroupM tiles of one segment; the short tiles of every segment
-// follow, in pairs.  Within each part all tiles run equally long, so the
+// rows and half the duration).  Full-duration tiles come first, in segment
+// order; a segment's n of them form ceil(n / 8) groups of nearly equal size
+// (a segment of up to 8 tiles is one group, so its weight slabs are fetched
+// once; with ntn N-tiles an M-tile's activations are then fetched about
+// ntn n / 32 times, which grows slower than the weights saved).  The short
+// tiles of every segment follow, in pairs.  Within each part all tiles run equally long, so the
 // workgroups that share an XCD's L2 stay in step: a short tile among full
 // ones frees its CU early, the tiles taken next start out of phase with
 // their neighbours, and the operand slices they would have shared are
@@ -74,10 +77,12 @@ __device__ __forceinline__ void build_tile_schedule(const int32_t* act, const in
     }
     int total;
     const int t0 = nfull_all + block_scan256(nf, &total, wsum);
+    const int ng = (nf + kGroupMax - 1) / kGroupMax;
+    const int g = ng > 0 ? (nf + ng - 1) / ng : 1;      // group size
     for (int j = 0; j < nf; ++j) {
       const int m = end - len + j * kTileM;
-      const int gs = t0 + j / kGroupM * kGroupM;
-      put(t0 + j, row, m, m + kTileM < end ? m + kTileM : end, gs, min(kGroupM, t0 + nf - gs));
+      const int gs = t0 + j / g * g;
+      put(t0 + j, row, m, m + kTileM < end ? m + kTileM : end, gs, min(g, t0 + nf - gs));
     }
     nfull_all += total;
   }
