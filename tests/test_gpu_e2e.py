@@ -21,7 +21,12 @@ SENT = 0x7F7F
 
 
 def _setup(w, target):
-    topk, rw = synth.routing(w, target)
+    # a float target is a maxvio of the workload's sweep; ("zipf", s) draws
+    # Zipf-biased routing of strength s directly (seed 7)
+    if isinstance(target, tuple):
+        topk, rw = synth.routing_zipf(w, target[1], seed=7)
+    else:
+        topk, rw = synth.routing(w, target)
     x = synth.hidden(w)
     home_h = [synth.expert_weights_host(w, i) for i in range(3)]
     return topk, rw, x, home_h
@@ -36,6 +41,9 @@ def _pool_dev(w):
     ("tiny_r4_s64_k2_e8", 1.0, None), ("tiny_r4_s64_k2_e8", 0.0, None),
     ("tiny_r4_s64_k2_e8", "adv", None),
     ("mid_r8_s1024_k4_e32", 0.0, [0, 5]), ("mid_r8_s1024_k4_e32", 2.0, [0, 3, 7]),
+    # maxvio 7: segments of 9 to 16 full tiles, split into uneven groups of up
+    # to 8 (rank 3: 15 and a short tail, rank 5: 16, rank 6: 9 and a tail)
+    ("mid_r8_s1024_k4_e32", ("zipf", 2.0), [3, 5, 6]),
 ])
 def test_ffn_matches_oracle(name, target, ranks):
     w = synth.WORKLOADS[name]

@@ -26,7 +26,10 @@ def _sentinel(shape):
 
 
 def _inputs(w, target, seed=5):
-    topk, _ = synth.routing(w, target)
+    if isinstance(target, tuple):                 # ("zipf", s): Zipf strength s, seed 7
+        topk, _ = synth.routing_zipf(w, target[1], seed=7)
+    else:
+        topk, _ = synth.routing(w, target)
     p = oracle.plan(topk, w.E, w.B, w.token_padding)
     x_nvs, _ = oracle.dispatch(p, synth.hidden(w))
     rng = np.random.default_rng(seed)
@@ -42,6 +45,7 @@ def _inputs(w, target, seed=5):
     ("tiny_r4_s64_k2_e8", 1.0, None), ("tiny_r4_s64_k2_e8", 0.0, None),
     ("tiny_r4_s64_k2_e8", "adv", None),
     ("mid_r8_s1024_k4_e32", 0.0, [0, 6]), ("mid_r8_s1024_k4_e32", 2.0, [1, 4]),
+    ("mid_r8_s1024_k4_e32", ("zipf", 2.0), [3, 6]),   # segments of 9-16 full tiles
 ])
 def test_ffn_bwd_matches_oracle(name, target, ranks):
     w = synth.WORKLOADS[name]
