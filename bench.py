@@ -437,9 +437,10 @@ def time_per_rank(w, buf, batches, home, pool, x, reps=3):
         buf.plan(topk, plan=plan)
         buf.dispatch(plan, x, rw, x_nvs=x_nvs)
         buf.prefetch_weight(plan, home, pool)
+        for d in range(w.R):                                               # warm every rank
+            buf.expert_ffn(plan, x_nvs, home, pool, z_ws=z, y_nvs=y, rank=d)
         ms = []
         for d in range(w.R):
-            buf.expert_ffn(plan, x_nvs, home, pool, z_ws=z, y_nvs=y, rank=d)   # warm
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             ev[0].record()
             for _ in range(reps):
