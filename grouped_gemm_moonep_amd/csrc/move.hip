@@ -144,65 +144,68 @@ struct CombineArgs {
 };
 
 
-// One wave per token.  The output row is built in column chunks of
-// 64 kCombVecs 16-byte vectors (7 KiB of a 7168-wide row): for each chunk the
-// K source rows are read whole, kCombRows at a time, and added in ascending k.
-// Reading each source row as one long contiguous piece instead of one
-// 16-byte vector of all K rows at a time measured 10% faster on the same
-// gather (5.79 against 5.28 TB/s).
-constexpr int kCombVecs = 7;
+// One wave per (token, column chunk of 64 kCombVecs 16-byte vectors = 3 KiB),
+// on a grid of one chunk per wave: the wave reads the chunk of the token's K
+// source rows, kCombRows rows at a time, and adds them in ascending k.
+// Contiguous pieces of each source row measured faster than one 16-byte
+// vector of all K rows at a time (5.79 against 5.28 TB/s on the same
+// gather), and one piece of work per wave on a large grid faster than a loop
+// (chunks of 7, 4 and 2 vectors and 3 or 4 rows in flight were within 2% of
+// this or slower).
+constexpr int kCombVecs = 3;
 constexpr int kCombRows = 2;      // source rows in flight
 
 template <bool kWeighted>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  for (int t = (int)blockIdx.x * kWaves + wv; t < a.ntok; t += gridDim.x * kWaves) {
-    const int tok = uniform(t);
+  const int nchunks = (a.nv + 64 * kCombVecs - 1) / (64 * kCombVecs);
+  const int64_t items = (int64_t)a.ntok * nchunks;
+  for (int64_t it = (int64_t)blockIdx.x * kWaves + wv; it < items; it += (int64_t)gridDim.x * kWaves) {
+    const int tok = uniform((int)(it / nchunks));
+    const int c0 = uniform((int)(it % nchunks)) * 64 * kCombVecs;
     const int32_t* dk = a.dest + (int64_t)tok * a.K;
     u32x4* dst = a.out + (int64_t)tok * a.nv;
-    for (int c0 = 0; c0 < a.nv; c0 += 64 * kCombVecs) {
-      float acc[kCombVecs][8];
-      for (int k0 = 0; k0 < a.K; k0 += kCombRows) {
-        const int kn = a.K - k0 < kCombRows ? a.K - k0 : kCombRows;
-        u32x4 yv[kCombRows][kCombVecs];
-        int slot[kCombRows];
+    float acc[kCombVecs][8];
+    for (int k0 = 0; k0 < a.K; k0 += kCombRows) {
+      const int kn = a.K - k0 < kCombRows ? a.K - k0 : kCombRows;
+      u32x4 yv[kCombRows][kCombVecs];
+      int slot[kCombRows];
 #pragma unroll
-        for (int r = 0; r < kCombRows; ++r) {
-          slot[r] = r < kn ? uniform(dk[k0 + r]) : 0;
+      for (int r = 0; r < kCombRows; ++r) {
+        slot[r] = r < kn ? uniform(dk[k0 + r]) : 0;
 #pragma unroll
-          for (int u = 0; u < kCombVecs; ++u) {
-            const int v = c0 + u * 64 + lane;
-            if (r < kn && v < a.nv) yv[r][u] = __builtin_nontemporal_load(a.y + (int64_t)slot[r] * a.nv + v);
-          }
+        for (int u = 0; u < kCombVecs; ++u) {
+          const int v = c0 + u * 64 + lane;
+          if (r < kn && v < a.nv) yv[r][u] = __builtin_nontemporal_load(a.y + (int64_t)slot[r] * a.nv + v);
         }
-#pragma unroll
-        for (int r = 0; r < kCombRows; ++r)
-          if (r < kn) {
-            const int k = k0 + r;
-            const float wk = kWeighted ? a.rw_nvs[slot[r]] : 1.0f;
-#pragma unroll
-            for (int u = 0; u < kCombVecs; ++u)
-#pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                const float pj0 = (j & 1) ? bf16_hi(yv[r][u][j >> 1]) : bf16_lo(yv[r][u][j >> 1]);
-                const float pj = kWeighted ? __fmul_rn(wk, pj0) : pj0;
-                acc[u][j] = (k == 0) ? pj : __fadd_rn(acc[u][j], pj);
-              }
-          }
       }
 #pragma unroll
-      for (int u = 0; u < kCombVecs; ++u) {
-        const int v = c0 + u * 64 + lane;
-        if (v < a.nv) {
-          u32x4 o;
+      for (int r = 0; r < kCombRows; ++r)
+        if (r < kn) {
+          const int k = k0 + r;
+          const float wk = kWeighted ? a.rw_nvs[slot[r]] : 1.0f;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = bf16_rne(acc[u][2 * j]) | (bf16_rne(acc[u][2 * j + 1]) << 16);
-          __builtin_nontemporal_store(o, dst + v);
+          for (int u = 0; u < kCombVecs; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float pj0 = (j & 1) ? bf16_hi(yv[r][u][j >> 1]) : bf16_lo(yv[r][u][j >> 1]);
+              const float pj = kWeighted ? __fmul_rn(wk, pj0) : pj0;
+              acc[u][j] = (k == 0) ? pj : __fadd_rn(acc[u][j], pj);
+            }
         }
+    }
+#pragma unroll
+    for (int u = 0; u < kCombVecs; ++u) {
+      const int v = c0 + u * 64 + lane;
+      if (v < a.nv) {
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = bf16_rne(acc[u][2 * j]) | (bf16_rne(acc[u][2 * j + 1]) << 16);
+        __builtin_nontemporal_store(o, dst + v);
       }
     }
-    if (kWeighted && a.rw_sk && lane < a.K)
+    if (kWeighted && a.rw_sk && c0 == 0 && lane < a.K)
       a.rw_sk[(int64_t)tok * a.K + lane] = a.rw_nvs[dk[lane]];
   }
 }
@@ -361,7 +364,8 @@ hipError_t launch_combine(const Ctx& c, const moonep_plan_t& p, const uint16_t* 
   CombineArgs a;
   a.y = (const u32x4*)y; a.rw_nvs = rw_nvs; a.out = (u32x4*)out; a.rw_sk = rw_sk;
   a.dest = p.dest; a.ntok = d.R * d.S; a.K = d.K; a.nv = W / 8;
-  const int blocks = capped_grid(c, (a.ntok + kWaves - 1) / kWaves);
+  const int nchunks = (a.nv + 64 * kCombVecs - 1) / (64 * kCombVecs);
+  const int blocks = capped_grid(c, ((int64_t)a.ntok * nchunks + kWaves - 1) / kWaves);
   if (rw_nvs)
     combine_kernel<true><<<blocks, kThreads, 0, s>>>(a);
   else
