@@ -28,7 +28,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 8;          // 16-byte vectors per lane in flight
-constexpr int kRowVecs = 16;        // 16-byte vectors per lane holding a whole row (W <= 8192)
+constexpr int kDispVecs = 16;       // 16-byte vectors per lane of one dispatch column chunk
 
 __device__ __forceinline__ int round_up(int n, int m) { return (n + m - 1) / m * m; }
 
@@ -56,14 +56,13 @@ struct DispatchArgs {
 };
 
 // Blocks [0, npad_blocks): zero the padding rows of one active row (one part
-// of it).  Blocks past that copy token rows to their slots.  When a row fits
-// in registers (kWhole), one wave per (token, k) pair reads the row and writes
-// it to that one slot, on a grid of one pair per wave: the K waves of a token
-// are neighbours and take the row from L2, and a write per wave on a large
-// grid measured 5% faster than one wave writing all K slots of its tokens
-// in a grid-stride loop (5.29 against 5.05 TB/s on the same scatter).
-// Otherwise one wave per token writes its K slots 8 KiB at a time.
-template <bool kWhole>
+// of it).  Blocks past that: one wave per (token, k) pair and column chunk of
+// 64 kDispVecs vectors (the whole row up to 8192 columns), on a grid of one
+// item per wave: the wave reads the chunk of the token's row and writes it to
+// the pair's slot.  The K waves of a token are neighbours and take the row
+// from L2.  One write per wave on a large grid measured 10-14% faster in the
+// kernel than one wave writing all K slots of its tokens in a grid-stride
+// loop; smaller chunks (7 or 4 vectors) were 15-50% slower.
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -86,51 +85,28 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs a) {
     return;
   }
   const int nblk = gridDim.x - a.npad_blocks;
-  if constexpr (kWhole) {
-    const int64_t npairs = (int64_t)a.ntok * a.K;
-    for (int64_t p = ((int64_t)blockIdx.x - a.npad_blocks) * kWaves + wv; p < npairs;
-         p += (int64_t)nblk * kWaves) {
-      const int tok = uniform((int)(p / a.K));
-      const int slot = uniform(a.dest[p]);
-      const u32x4* src = a.x + (int64_t)tok * a.nv;
-      u32x4* dst = a.x_nvs + (int64_t)slot * a.nv;
-      u32x4 buf[kRowVecs];
-#pragma unroll
-      for (int u = 0; u < kRowVecs; ++u) {
-        const int v = u * 64 + lane;
-        if (v < a.nv) buf[u] = src[v];
-      }
-#pragma unroll
-      for (int u = 0; u < kRowVecs; ++u) {
-        const int v = u * 64 + lane;
-        if (v < a.nv) dst[v] = buf[u];
-      }
-      if (a.rw && lane == 0) a.rw_nvs[slot] = a.rw[p];
-    }
-    return;
-  }
-  for (int t = ((int)blockIdx.x - a.npad_blocks) * kWaves + wv; t < a.ntok;
-       t += nblk * kWaves) {
-    const int tok = uniform(t);
+  const int nch = (a.nv + 64 * kDispVecs - 1) / (64 * kDispVecs);   // column chunks per row
+  const int64_t items = (int64_t)a.ntok * a.K * nch;
+  for (int64_t it = ((int64_t)blockIdx.x - a.npad_blocks) * kWaves + wv; it < items;
+       it += (int64_t)nblk * kWaves) {
+    const int64_t p = it / nch;                           // (token, k) pair
+    const int c0 = uniform((int)(it - p * nch)) * 64 * kDispVecs;
+    const int tok = uniform((int)(p / a.K));
+    const int slot = uniform(a.dest[p]);
     const u32x4* src = a.x + (int64_t)tok * a.nv;
-    const int32_t* dk = a.dest + (int64_t)tok * a.K;
-    for (int base = 0; base < a.nv; base += 64 * kUnroll) {
-      u32x4 buf[kUnroll];
+    u32x4* dst = a.x_nvs + (int64_t)slot * a.nv;
+    u32x4 buf[kDispVecs];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int v = base + u * 64 + lane;
-        if (v < a.nv) buf[u] = __builtin_nontemporal_load(src + v);
-      }
-      for (int k = 0; k < a.K; ++k) {
-        u32x4* dst = a.x_nvs + (int64_t)uniform(dk[k]) * a.nv;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int v = base + u * 64 + lane;
-          if (v < a.nv) dst[v] = buf[u];
-        }
-      }
+    for (int u = 0; u < kDispVecs; ++u) {
+      const int v = c0 + u * 64 + lane;
+      if (v < a.nv) buf[u] = src[v];
     }
-    if (a.rw && lane < a.K) a.rw_nvs[dk[lane]] = a.rw[(int64_t)tok * a.K + lane];
+#pragma unroll
+    for (int u = 0; u < kDispVecs; ++u) {
+      const int v = c0 + u * 64 + lane;
+      if (v < a.nv) dst[v] = buf[u];
+    }
+    if (a.rw && c0 == 0 && lane == 0) a.rw_nvs[slot] = a.rw[p];
   }
 }
 
@@ -348,13 +324,9 @@ hipError_t launch_dispatch(const Ctx& c, const moonep_plan_t& p, const uint16_t*
   a.tp = d.tp; a.NvS = (int)d.NvS;
   a.pad_parts = (d.tp + 4 * kWaves - 1) / (4 * kWaves);
   a.npad_blocks = d.R * a.L2 * a.pad_parts;
-  if (a.nv <= 64 * kRowVecs) {
-    const int pair_blocks = capped_grid(c, ((int64_t)a.ntok * a.K + kWaves - 1) / kWaves);
-    dispatch_kernel<true><<<a.npad_blocks + pair_blocks, kThreads, 0, s>>>(a);
-  } else {
-    const int tok_blocks = capped_grid(c, (a.ntok + kWaves * 2 - 1) / (kWaves * 2));
-    dispatch_kernel<false><<<a.npad_blocks + tok_blocks, kThreads, 0, s>>>(a);
-  }
+  const int nch = (a.nv + 64 * kDispVecs - 1) / (64 * kDispVecs);
+  const int item_blocks = capped_grid(c, ((int64_t)a.ntok * a.K * nch + kWaves - 1) / kWaves);
+  dispatch_kernel<<<a.npad_blocks + item_blocks, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
