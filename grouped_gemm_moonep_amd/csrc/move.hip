@@ -186,7 +186,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   }
 }
 
-// prefetch: work item = (used slot, projection, chunk of a row).
+// prefetch: workgroup = (projection, 16 KiB column chunk of a weight row); it
+// copies that chunk of every used slot in turn, so at any moment the
+// workgroups sweep the rows of one slot together (a moving window, which
+// measured 3-8% faster than each workgroup streaming its own 256 KiB piece).
 struct PrefetchArgs {
   const u32x4* home[3];  // home row e of rank d at home + (d*hstride + e) rows
   u32x4* pool[3];        // slot j of rank d at pool + (d*pstride + j) rows
@@ -196,32 +199,33 @@ struct PrefetchArgs {
   int64_t row_vecs;
   int64_t hstride, pstride;
   int B;
-  int chunk_vecs, nchunks;
+  int nchunks;           // 16 KiB chunks per row
 };
+
+constexpr int kPrefetchVecs = 4;   // 16-byte vectors per thread of one chunk
 
 __global__ __launch_bounds__(kThreads) void prefetch_kernel(PrefetchArgs a) {
   const int n = *a.aux_pf_n;
-  const int64_t items = (int64_t)n * 3 * a.nchunks;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int chunk = (int)(it % a.nchunks);
-    const int proj = (int)((it / a.nchunks) % 3);
-    const int q = (int)(it / ((int64_t)a.nchunks * 3));
-    const int slot = a.aux_pf[q];
-    const int e = a.pf[slot];
-    const int d = slot / a.B;
-    const u32x4* src = a.home[proj] + ((int64_t)d * a.hstride + e) * a.row_vecs;
-    u32x4* dst = a.pool[proj] + ((int64_t)d * a.pstride + slot - d * a.B) * a.row_vecs;
-    const int64_t v0 = (int64_t)chunk * a.chunk_vecs;
-    int64_t v1 = v0 + a.chunk_vecs;
-    if (v1 > a.row_vecs) v1 = a.row_vecs;
-    for (int64_t v = v0 + threadIdx.x; v < v1; v += kThreads * 4) {
-      u32x4 b[4];
+  const int proj = blockIdx.x % 3;
+  for (int ch = blockIdx.x / 3; ch < a.nchunks; ch += gridDim.x / 3) {
+    const int64_t v0 = (int64_t)ch * (kThreads * kPrefetchVecs) + threadIdx.x;
+    for (int q = 0; q < n; ++q) {
+      const int slot = a.aux_pf[q];
+      const int e = a.pf[slot];
+      const int d = slot / a.B;
+      const u32x4* src = a.home[proj] + ((int64_t)d * a.hstride + e) * a.row_vecs;
+      u32x4* dst = a.pool[proj] + ((int64_t)d * a.pstride + slot - d * a.B) * a.row_vecs;
+      u32x4 b[kPrefetchVecs];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (v + u * kThreads < v1) b[u] = __builtin_nontemporal_load(src + v + u * kThreads);
+      for (int u = 0; u < kPrefetchVecs; ++u) {
+        const int64_t v = v0 + u * kThreads;
+        if (v < a.row_vecs) b[u] = __builtin_nontemporal_load(src + v);
+      }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (v + u * kThreads < v1) __builtin_nontemporal_store(b[u], dst + v + u * kThreads);
+      for (int u = 0; u < kPrefetchVecs; ++u) {
+        const int64_t v = v0 + u * kThreads;
+        if (v < a.row_vecs) __builtin_nontemporal_store(b[u], dst + v);
+      }
     }
   }
 }
@@ -371,11 +375,9 @@ hipError_t launch_prefetch(const Ctx& c, const moonep_plan_t& p, const WeightRef
   a.aux_pf = p.aux + d.aux.pf;
   a.aux_pf_n = p.aux + d.aux.pf_n;
   a.row_vecs = (int64_t)d.H * d.Hp / 8;
-  a.chunk_vecs = kThreads * 4 * 16;   // 256 KiB per work item
-  a.nchunks = (int)((a.row_vecs + a.chunk_vecs - 1) / a.chunk_vecs);
-  const int64_t max_items = (int64_t)d.R * d.B * 3 * a.nchunks;
-  const int blocks = capped_grid(c, max_items < (int64_t)c.num_cu_device * 8
-                                        ? max_items : (int64_t)c.num_cu_device * 8);
+  a.nchunks = (int)((a.row_vecs + kThreads * kPrefetchVecs - 1) / (kThreads * kPrefetchVecs));
+  // three workgroups (projections) per chunk; a CU budget makes them loop over chunks
+  const int blocks = capped_grid(c, 3LL * a.nchunks) / 3 * 3;
   prefetch_kernel<<<blocks, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }

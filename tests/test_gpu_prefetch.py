@@ -11,16 +11,17 @@ from gpu_util import buffer_for, dev, dev_bf16, host_bf16, log
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,target", [
-    ("tiny_r4_s64_k2_e8", 1.0), ("tiny_r4_s64_k2_e8", "adv"),
-    ("mid_r8_s1024_k4_e32", 2.0), ("mid_r8_s1024_k4_e32", 0.0),
-    ("infer_r8_s128_k8_e256_b4", 4.0)])
-def test_prefetch_rows_equal_home_rows(name, target):
+@pytest.mark.parametrize("name,target,num_cus", [
+    ("tiny_r4_s64_k2_e8", 1.0, 0), ("tiny_r4_s64_k2_e8", "adv", 0),
+    ("mid_r8_s1024_k4_e32", 2.0, 0), ("mid_r8_s1024_k4_e32", 0.0, 0),
+    ("mid_r8_s1024_k4_e32", 2.0, 3),                   # CU budget: workgroups loop over chunks
+    ("infer_r8_s128_k8_e256_b4", 4.0, 0)])
+def test_prefetch_rows_equal_home_rows(name, target, num_cus):
     w = synth.WORKLOADS[name]
-    log(f"prefetch {name} target={target}")
+    log(f"prefetch {name} target={target} num_cus={num_cus}")
     topk, _ = synth.routing(w, target)
     p = oracle.plan(topk, w.E, w.B, w.token_padding)
-    buf = buffer_for(w)
+    buf = buffer_for(w, num_cus=num_cus)
     plan = buf.plan(dev(topk))
     if w.H * w.Hp * w.E <= 1 << 26:
         home_h = [synth.expert_weights_host(w, i) for i in range(3)]
