@@ -28,6 +28,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 8;          // 16-byte vectors per lane in flight
+constexpr int kXcdsMove = 8;       // XCDs: workgroup b runs on XCD b mod 8
 constexpr int kDispVecs = 16;       // 16-byte vectors per lane of one dispatch column chunk
 
 __device__ __forceinline__ int round_up(int n, int m) { return (n + m - 1) / m * m; }
@@ -52,21 +53,24 @@ struct DispatchArgs {
   const int32_t* cu;     // [R][E+B]
   const int32_t* segn;   // [R][E+B]
   const int32_t* act;    // [R][2L]
-  int ntok, K, nv, EB, L2, tp, pad_parts, npad_blocks, NvS;
+  int ntok, K, nv, EB, L2, tp, pad_parts, npad_blocks, npad_used, NvS;
+  int xcd_local;          // 1: the grid has one item per wave, a token's waves on one XCD
 };
 
 // Blocks [0, npad_blocks): zero the padding rows of one active row (one part
 // of it).  Blocks past that: one wave per (token, k) pair and column chunk of
 // 64 kDispVecs vectors (the whole row up to 8192 columns), on a grid of one
 // item per wave: the wave reads the chunk of the token's row and writes it to
-// the pair's slot.  The K waves of a token are neighbours and take the row
-// from L2.  One write per wave on a large grid measured 10-14% faster in the
-// kernel than one wave writing all K slots of its tokens in a grid-stride
-// loop; smaller chunks (7 or 4 vectors) were 15-50% slower.
+// the pair's slot.  The workgroups of a token run on one XCD, so its K waves
+// take the row from that XCD's L2 (HBM reads 0.96 -> 0.48 GB at the headline,
+// 1% faster).  One write per wave on a large grid measured 10-14% faster in
+// the kernel than one wave writing all K slots of its tokens in a
+// grid-stride loop; smaller chunks (7 or 4 vectors) were 15-50% slower.
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   if ((int)blockIdx.x < a.npad_blocks) {
+    if ((int)blockIdx.x >= a.npad_used) return;        // rounding of the padding blocks
     const int part = blockIdx.x % a.pad_parts;
     const int dq = blockIdx.x / a.pad_parts;        // d * 2L + q
     const int row = a.act[dq];
@@ -86,9 +90,27 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs a) {
   }
   const int nblk = gridDim.x - a.npad_blocks;
   const int nch = (a.nv + 64 * kDispVecs - 1) / (64 * kDispVecs);   // column chunks per row
-  const int64_t items = (int64_t)a.ntok * a.K * nch;
-  for (int64_t it = ((int64_t)blockIdx.x - a.npad_blocks) * kWaves + wv; it < items;
-       it += (int64_t)nblk * kWaves) {
+  const int per_tok = a.K * nch;                          // items of a token
+  int64_t it, step, items;
+  if (a.xcd_local) {
+    // the wpt workgroups of token t are t's group of 8 tokens x wpt, at the
+    // position of t in its group: all on XCD t mod 8 (npad_blocks is a
+    // multiple of 8), so the K reads of its row share that XCD's L2
+    const int wpt = (per_tok + kWaves - 1) / kWaves;
+    const int b = (int)blockIdx.x - a.npad_blocks;
+    const int c = b / kXcdsMove;
+    const int tok = (c / wpt) * kXcdsMove + b % kXcdsMove;
+    const int item = (c % wpt) * kWaves + wv;
+    if (tok >= a.ntok || item >= per_tok) return;
+    it = (int64_t)tok * per_tok + item;
+    step = 0;
+    items = it + 1;
+  } else {
+    it = ((int64_t)blockIdx.x - a.npad_blocks) * kWaves + wv;
+    step = (int64_t)nblk * kWaves;
+    items = (int64_t)a.ntok * per_tok;
+  }
+  for (; it < items; it += step) {
     const int64_t p = it / nch;                           // (token, k) pair
     const int c0 = uniform((int)(it - p * nch)) * 64 * kDispVecs;
     const int tok = uniform((int)(p / a.K));
@@ -107,6 +129,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs a) {
       if (v < a.nv) dst[v] = buf[u];
     }
     if (a.rw && c0 == 0 && lane == 0) a.rw_nvs[slot] = a.rw[p];
+    if (step == 0) break;
   }
 }
 
@@ -327,9 +350,13 @@ hipError_t launch_dispatch(const Ctx& c, const moonep_plan_t& p, const uint16_t*
   a.ntok = d.R * d.S; a.K = d.K; a.nv = W / 8; a.EB = d.E + d.B; a.L2 = 2 * d.L;
   a.tp = d.tp; a.NvS = (int)d.NvS;
   a.pad_parts = (d.tp + 4 * kWaves - 1) / (4 * kWaves);
-  a.npad_blocks = d.R * a.L2 * a.pad_parts;
+  a.npad_used = d.R * a.L2 * a.pad_parts;
+  a.npad_blocks = (a.npad_used + kXcdsMove - 1) / kXcdsMove * kXcdsMove;
   const int nch = (a.nv + 64 * kDispVecs - 1) / (64 * kDispVecs);
-  const int item_blocks = capped_grid(c, ((int64_t)a.ntok * a.K * nch + kWaves - 1) / kWaves);
+  const int64_t wpt = ((int64_t)a.K * nch + kWaves - 1) / kWaves;
+  const int64_t want = (a.ntok + kXcdsMove - 1) / kXcdsMove * kXcdsMove * wpt;
+  const int item_blocks = capped_grid(c, want);
+  a.xcd_local = item_blocks == want ? 1 : 0;     // a CU budget falls back to a grid-stride loop
   dispatch_kernel<<<a.npad_blocks + item_blocks, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
