@@ -29,6 +29,11 @@ bool dims_from_config(const moonep_config_t* cfg, Dims* out) {
   if ((int64_t)c.R * nvs >= (int64_t(1) << 31)) return false;
   const int64_t wmax = c.H > c.Hp ? c.H : c.Hp;
   if ((int64_t)c.R * nvs * wmax >= (int64_t(1) << 40)) return false;
+  // The GEMM kernels address a weight row (H x H' bf16) and a segment's
+  // operand rows (at most S*K rows of H or H' bf16) through one buffer
+  // descriptor each, whose offsets are 31 bits.
+  if ((int64_t)c.H * c.Hp * 2 >= (int64_t(1) << 31)) return false;
+  if ((int64_t)c.S * c.K * wmax * 2 >= (int64_t(1) << 31)) return false;
   Dims d;
   d.R = c.R; d.S = c.S; d.K = c.K; d.E = c.E; d.B = c.B; d.H = c.H;
   d.Hp = c.Hp; d.tp = c.token_padding; d.num_cus = c.num_cus;
