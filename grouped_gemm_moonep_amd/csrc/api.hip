@@ -24,6 +24,7 @@ bool dims_from_config(const moonep_config_t* cfg, Dims* out) {
   if ((int64_t)c.R * (c.E + c.B) > kMaxRE) return false;
   if (c.token_padding < 1) return false;
   if (c.H < 64 || c.H % 64 || c.Hp < 64 || c.Hp % 64) return false;
+  if (c.H > 65536 || c.Hp > 65536) return false;   // a tile's lane offsets stay below 2^26
   if (c.num_cus < 0) return false;
   const int64_t nvs = (int64_t)c.S * c.K + 2LL * L * c.token_padding;
   if ((int64_t)c.R * nvs >= (int64_t(1) << 31)) return false;

@@ -59,7 +59,7 @@ enum {
  * upper bound on their workgroups in flight (the README's num_sms knob).
  * Supported: 1 <= R <= 64, E % R == 0, E <= 1024, R*E <= 16384, 1 <= K <= min(E, 32),
  * 1 <= S, R*S*K < 2^31, 0 <= B <= E/R, R*(E+B) <= 16384,
- * token_padding >= 1, H % 64 == 0, Hp % 64 == 0, R*NvS*max(H,Hp) < 2^40,
+ * token_padding >= 1, H % 64 == 0, Hp % 64 == 0, H, Hp <= 65536, R*NvS*max(H,Hp) < 2^40,
  * H*Hp < 2^30 and S*K*max(H,Hp) < 2^30 (the GEMMs address one weight row and
  * one segment's operand rows with 31-bit buffer offsets). */
 typedef struct {

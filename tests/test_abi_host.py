@@ -62,7 +62,8 @@ BAD = [dict(E=6, R=4), dict(K=0), dict(K=9, E=8), dict(B=3), dict(B=-1), dict(S=
        dict(token_padding=0), dict(H=100), dict(Hp=32), dict(R=65, E=130), dict(E=2048, R=2),
        dict(num_cus=-1), dict(K=33, E=64),
        dict(H=32768, Hp=32768),                 # a weight row past 31-bit offsets
-       dict(S=1 << 16, K=2, H=8192, Hp=64)]     # a segment past 31-bit offsets
+       dict(S=1 << 16, K=2, H=8192, Hp=64),     # a segment past 31-bit offsets
+       dict(H=65536 + 64, Hp=64)]
 
 
 @pytest.mark.parametrize("bad", BAD)
