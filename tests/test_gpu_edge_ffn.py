@@ -30,6 +30,9 @@ SHAPES = [
     synth.Workload("e_b0", R=4, S=257, K=2, E=16, B=0, H=128, Hp=128, token_padding=16),
     synth.Workload("e_s1", R=3, S=1, K=2, E=6, B=2, H=64, Hp=192, token_padding=2),
     synth.Workload("e_tails", R=2, S=700, K=2, E=4, B=2, H=448, Hp=320, token_padding=1),
+    # padding granularities above the 128-row short tile: segment tails of any length
+    synth.Workload("e_tp200", R=2, S=300, K=2, E=4, B=2, H=128, Hp=192, token_padding=200),
+    synth.Workload("e_tp384", R=4, S=200, K=3, E=8, B=2, H=192, Hp=128, token_padding=384),
 ]
 
 

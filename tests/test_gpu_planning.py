@@ -76,6 +76,7 @@ EDGE = [
     synth.Workload("l1", R=16, S=200, K=4, E=16, B=1, H=64, Hp=64, token_padding=8),
     synth.Workload("wide", R=8, S=600, K=8, E=1024, B=128, H=64, Hp=64, token_padding=32),
     synth.Workload("r64", R=64, S=40, K=2, E=128, B=2, H=64, Hp=64, token_padding=4),
+    synth.Workload("tp384", R=4, S=200, K=3, E=8, B=2, H=64, Hp=64, token_padding=384),
 ]
 
 
