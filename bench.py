@@ -93,27 +93,34 @@ def down_flops(w):
 
 
 TRAFFIC_FILE = os.path.join(REPO, "profiles", "traffic_ffn_gateup_fwd_r8_s4096_k8_e256.txt")
-KERNEL_SOURCES = [os.path.join(REPO, "grouped_gemm_moonep_amd", "csrc", f)
-                  for f in ("gemm_core.h", "gemm.hip")]
+_CSRC = os.path.join(REPO, "grouped_gemm_moonep_amd", "csrc")
+# kernel -> (hash key, sources the counters are valid for, bytes key) in TRAFFIC_FILE
+TRAFFIC_KEYS = {
+    "ffn_gateup": ("source_sha256", ("gemm_core.h", "gemm.hip"), "hbm_bytes_per_launch"),
+    "ffn_down": ("source_sha256", ("gemm_core.h", "gemm.hip"), "down_hbm_bytes_per_launch"),
+    "dispatch": ("move_source_sha256", ("move.hip",), "dispatch_hbm_bytes_per_launch"),
+    "combine": ("move_source_sha256", ("move.hip",), "combine_hbm_bytes_per_launch"),
+}
 
 
-def measured_traffic():
-    """HBM bytes per ffn_gateup launch from the committed counter summary, or
-    None when the kernel's sources (gemm_core.h, gemm.hip) have changed since
-    the counters were taken."""
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` (a TRAFFIC_KEYS name) from the
+    committed counter summary of the headline workload, or None when the
+    kernel's sources have changed since the counters were taken."""
     import hashlib
+    hkey, sources, bkey = TRAFFIC_KEYS[kernel]
     try:
         fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE)
                       if ":" in line and not line.startswith(" "))
         h = hashlib.sha256()
-        for f in KERNEL_SOURCES:
-            h.update(open(f, "rb").read())
+        for f in sources:
+            h.update(open(os.path.join(_CSRC, f), "rb").read())
         src = h.hexdigest()
     except OSError:
         return None
-    if fields.get("source_sha256", "").strip() != src:
+    if fields.get(hkey, "").strip() != src or bkey not in fields:
         return None
-    return int(fields["hbm_bytes_per_launch"].strip())
+    return int(fields[bkey].strip())
 
 
 def cpu_baseline(w, host_routing, main_target, chunk=1024):
@@ -645,17 +652,20 @@ def main():
         "roofline": {**ffn_roofline(
             f"ffn_gateup (gate and up GEMMs + SwiGLU, all {w.R} ranks, one launch)",
             gateup_flops(w), gu_bytes, t_gu),
-            "traffic": measured_traffic() if w.name == WORKLOAD else None},
+            "traffic": measured_traffic("ffn_gateup") if w.name == WORKLOAD else None},
         "roofline_down": {**ffn_roofline(f"ffn_down (down GEMM, all {w.R} ranks, one launch)",
-                                         down_flops(w), dn_bytes, t_dn), "traffic": None},
+                                         down_flops(w), dn_bytes, t_dn),
+                          "traffic": measured_traffic("ffn_down") if w.name == WORKLOAD else None},
         "roofline_dispatch": {"bound": "hbm", "achieved": round(db / t_disp / 1e9, 1),
                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(db / t_disp / 1e9 / HBM_PEAK_GBS, 4),
-                              "traffic": None, "per_launch": {"bytes": db, "avg_s": t_disp}},
+                              "traffic": measured_traffic("dispatch") if w.name == WORKLOAD else None,
+                              "per_launch": {"bytes": db, "avg_s": t_disp}},
         "roofline_combine": {"bound": "hbm", "achieved": round(cb / t_comb / 1e9, 1),
                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(cb / t_comb / 1e9 / HBM_PEAK_GBS, 4),
-                             "traffic": None, "per_launch": {"bytes": cb, "avg_s": t_comb}},
+                             "traffic": measured_traffic("combine") if w.name == WORKLOAD else None,
+                             "per_launch": {"bytes": cb, "avg_s": t_comb}},
         "sweep": sweep,
     }
     if not args.no_per_rank:
