@@ -1,5 +1,5 @@
 """Host-side logic of bench.py (no GPU): the one-GPU guard and the choice of
-the binding roofline for the grouped GEMM."""
+the binding roofline for the grouped GEMM, and the counter-measured traffic."""
 import os
 import subprocess
 import sys
@@ -41,3 +41,31 @@ def test_algorithmic_bytes_scale_with_the_row_width():
     assert d == pytest.approx(ntok * 2 * w.H * (1 + w.K), rel=0.01)
     assert c == pytest.approx(ntok * 2 * w.H * (1 + w.K), rel=0.01)
     assert p == 8 * ntok * w.K + 4 * w.R * (w.E + w.B)
+
+
+def test_measured_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
+    """Counter figures are reported only while the kernel sources they were
+    taken with are unchanged (one hash for the GEMMs, one for data movement)."""
+    import hashlib
+    import bench
+    csrc = tmp_path / "csrc"
+    csrc.mkdir()
+    for f, text in (("gemm_core.h", "a"), ("gemm.hip", "b"), ("move.hip", "c")):
+        (csrc / f).write_text(text)
+    gemm = hashlib.sha256(b"ab").hexdigest()
+    move = hashlib.sha256(b"c").hexdigest()
+    summary = tmp_path / "traffic.txt"
+    summary.write_text(f"header: text\nsource_sha256: {gemm}\nhbm_bytes_per_launch: 123\n"
+                       f"down_hbm_bytes_per_launch: 45\nmove_source_sha256: {move}\n"
+                       f"dispatch_hbm_bytes_per_launch: 6\ncombine_hbm_bytes_per_launch: 7\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(summary))
+    monkeypatch.setattr(bench, "_CSRC", str(csrc))
+    got = {k: bench.measured_traffic(k) for k in ("ffn_gateup", "ffn_down", "dispatch", "combine")}
+    assert got == {"ffn_gateup": 123, "ffn_down": 45, "dispatch": 6, "combine": 7}
+    (csrc / "move.hip").write_text("changed")
+    assert bench.measured_traffic("dispatch") is None and bench.measured_traffic("combine") is None
+    assert bench.measured_traffic("ffn_gateup") == 123
+    (csrc / "gemm.hip").write_text("changed")
+    assert bench.measured_traffic("ffn_gateup") is None and bench.measured_traffic("ffn_down") is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.txt"))
+    assert bench.measured_traffic("ffn_gateup") is None
