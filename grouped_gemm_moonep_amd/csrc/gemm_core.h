@@ -64,7 +64,6 @@ constexpr int kHalfTileM = kShortTileM;           // rows of a segment's short l
 static_assert(BM == kTileM && kGemmTileM == kTileM, "one M-tile height everywhere");
 constexpr int kXcds = 8;
 constexpr int kLoadsPerStep = 8;                  // LDS-DMA loads per wave per tile and step
-constexpr int kTileOffB = 0;                      // B tile offset inside its slot
 
 typedef __attribute__((address_space(3))) char lds_t;
 
@@ -124,11 +123,6 @@ __device__ __forceinline__ void load_lds(const DmaRsrc& r, lds_t* dst, uint32_t 
                : "v"(voff), "s"(r.v), "{m0}"(m0)
                : "memory");
 }
-// Stores past num_records are dropped: the epilogues need no branches.
-__device__ __forceinline__ void bstore16(Rsrc r, uint32_t voff, unsigned v) {
-  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, voff, 0, 0);
-}
-
 // ---------------------------------------------------------------------------
 // Operand tiles in LDS: 256 rows (or columns) x 64 k of bf16 = 32 KiB, one
 // per ring slot.
