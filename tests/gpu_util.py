@@ -74,6 +74,15 @@ def assert_close_bf16(got_bits, want_bits, rel=1e-2, abs_=2e-2, what="", ulps=1)
     bound = np.maximum(abs_, ulps * bf16_ulp(want_bits))
     m = float(err.max()) if g.size else 0.0
     worst = float((err / bound).max()) if g.size else 0.0
+    # the plain element-wise figures, so that the ulp allowance cannot hide a
+    # drift: how many elements exceed 2e-2 at all, and the mean signed error
+    # against the reference's rms (a bias, which independent rounding keeps
+    # near zero)
+    n_over = int((err > abs_).sum())
+    bias = float(np.mean(g - w) / max(np.sqrt(np.mean(w * w)), 1e-30)) if g.size else 0.0
+    log(f"{what}: rel-L2 {r:.2e} max-abs {m:.2e} above {abs_:g}: {n_over}/{g.size} "
+        f"bias/rms {bias:+.1e}")
     assert r <= rel and worst <= 1.0, \
         f"{what}: rel-L2 {r:.3e} max-abs {m:.3e} (worst err/bound {worst:.2f})"
+    assert abs(bias) <= 1e-3, f"{what}: systematic error, mean/rms {bias:.3e}"
     return r, m

@@ -98,8 +98,9 @@ def test_dispatch_full_size_sampled(name, target):
 def test_copy_mode_equals_zero_copy(target):
     """zero_copy=False (README "API guide > zero_copy"): dispatch into the
     Buffer's communication buffer and copy the used slots out; combine copies
-    its input in first.  Same bits as the zero-copy calls on every used slot;
-    rows past the last segment of the destination are left alone."""
+    its input in first.  Same bits as the zero-copy calls and as the oracle's
+    dispatch and combine on every used slot; rows past the last segment of the
+    destination are left alone."""
     w = synth.WORKLOADS["mid_r8_s1024_k4_e32"]
     topk, rw = synth.routing(w, target)
     p = oracle.plan(topk, w.E, w.B, w.token_padding)
@@ -117,7 +118,17 @@ def test_copy_mode_equals_zero_copy(target):
         assert (bh[d, end:] == SENTINEL).all()
         # rw_nvs past the last segment is not written by either call
         assert np.array_equal(rah[d, :end], rbh[d, :end])
+    # both modes against the oracle's dispatch of the same inputs
+    want, want_rw = oracle.dispatch(p, synth.hidden(w), rw)
+    for d in range(w.R):
+        end = p.cu_seqlens[d, -1]
+        assert np.array_equal(bh[d, :end], want[d, :end]), f"copy mode rank {d} rows"
+        assert np.array_equal(rbh[d, :end], want_rw[d, :end].view(np.uint32)), f"rank {d} rw"
     o1, g1 = buf.combine(plan, a, ra)
     o2, g2 = buf.combine(plan, b, rb, zero_copy=False)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(g1, g2)
+    # copy-mode combine of the copy-mode dispatch against the oracle's combine
+    out_want, rw_want = oracle.combine(p, want, want_rw)
+    assert np.array_equal(host_bf16(o2), out_want)
+    assert np.array_equal(g2.cpu().numpy().view(np.uint32), rw_want.view(np.uint32))
     buf.destroy()

@@ -5,7 +5,9 @@
 * slots outside segments are not written; y may alias x (in place);
 * plan -> dispatch -> prefetch -> FFN -> combine against the dense,
   unbalanced per-token MoE (no planner involved) at the same tolerance;
-* the full-size forward config checked on sampled rows of sampled segments.
+* the full-size forward config checked on sampled rows of sampled segments
+  (balanced, Zipf and adversarial routing) and end to end on sampled tokens
+  against the dense MoE.
 """
 import numpy as np
 import pytest
@@ -148,12 +150,18 @@ def test_inference_overflow_forward():
     buf.destroy()
 
 
-@pytest.mark.parametrize("name,target", [("fwd_r8_s4096_k8_e256", 2.0),
+@pytest.mark.parametrize("name,target", [("fwd_r8_s4096_k8_e256", 0.0),
+                                         ("fwd_r8_s4096_k8_e256", 2.0),
+                                         ("fwd_r8_s4096_k8_e256", "adv"),
                                          ("infer_r8_s128_k8_e256_b4", 4.0),
                                          ("pages_r8_s8192_k8_e384", 10.0)])
 def test_ffn_full_size_sampled(name, target):
     """Full-size weights drawn on the GPU; the oracle recomputes sampled rows
-    of sampled segments token by token from the home weights."""
+    of sampled segments token by token from the home weights.  At the
+    headline: balanced routing (whole 256-row tiles, no padding), Zipf
+    routing at maxvio 2, and the adversarial case, where each rank holds one
+    32768-row segment that the tile schedule splits into 16 groups of 8
+    tiles (rows sampled across the whole segment)."""
     w = synth.WORKLOADS[name]
     log(f"ffn full size {name} target={target}")
     topk, rw = synth.routing(w, target)
@@ -178,12 +186,60 @@ def test_ffn_full_size_sampled(name, target):
         e = row if row < w.E else p.prefetch_src[d, row - w.E]
         end = p.cu_seqlens[d, row]
         start = end - p.seg_len[d, row]
-        slots = start + rng.choice(p.seg_tokens[d, row], min(16, p.seg_tokens[d, row]), replace=False)
+        n_pick = min(64 if p.seg_tokens[d, row] > 4096 else 16, p.seg_tokens[d, row])
+        slots = start + rng.choice(p.seg_tokens[d, row], n_pick, replace=False)
         toks = p.src[d, slots] // w.K
         wts = [host_bf16(home[i][e]) for i in range(3)]
         zw, yw = oracle.ffn_token(xs[toks], *wts)
         assert_close_bf16(host_bf16(z[d, slots]), zw, what=f"z d={d} row={row}")
         assert_close_bf16(host_bf16(y[d, slots]), yw, what=f"y d={d} row={row}")
+    buf.destroy()
+
+
+class _DeviceRows:
+    """home[e] of a device weight tensor, copied to the host on first use (the
+    dense reference needs only the experts of the sampled tokens)."""
+
+    def __init__(self, t):
+        self.t, self.cache = t, {}
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            self.cache[e] = host_bf16(self.t[e])
+        return self.cache[e]
+
+
+@pytest.mark.parametrize("target,ntok", [("adv", 64), (0.0, 3), (2.0, 3)])
+def test_forward_full_size_equals_dense_sampled(target, ntok):
+    """The headline forward end to end (plan -> dispatch -> prefetch -> FFN in
+    place -> weighted combine, all 8 ranks at full size) on sampled tokens
+    against the dense per-token MoE, which never sees the plan; the gathered
+    route weights bit-exact for every token."""
+    w = synth.WORKLOADS["fwd_r8_s4096_k8_e256"]
+    log(f"forward full size {w.name} target={target}")
+    topk, rw = synth.routing(w, target)
+    home = [torch.empty((w.E, w.H, w.Hp), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    for i in range(3):
+        synth.expert_weights_device(w, i, home[i])
+    pool = _pool_dev(w)
+    g = torch.Generator(device="cuda").manual_seed(13)
+    x = torch.randn((w.R, w.S, w.H), generator=g, device="cuda").to(torch.bfloat16)
+    buf = buffer_for(w)
+    plan = buf.plan(dev(topk))
+    x_nvs, rw_nvs = buf.dispatch(plan, x, dev(rw))
+    buf.prefetch_weight(plan, home, pool)
+    buf.expert_ffn(plan, x_nvs, home, pool, y_nvs=x_nvs)
+    out, rw_sk = buf.combine(plan, x_nvs, rw_nvs)
+    torch.cuda.synchronize()
+    assert np.array_equal(rw_sk.cpu().numpy(), rw)
+    rows = np.random.default_rng(14).choice(w.R * w.S, ntok, replace=False)
+    r_, s_ = rows // w.S, rows % w.S
+    xh = host_bf16(x[torch.from_numpy(r_).cuda(), torch.from_numpy(s_).cuda()])
+    want = oracle.dense_moe(topk[r_, s_][None], rw[r_, s_][None], xh[None],
+                            [_DeviceRows(t) for t in home])[0]
+    got = host_bf16(out[torch.from_numpy(r_).cuda(), torch.from_numpy(s_).cuda()])
+    assert_close_bf16(got, want, what=f"forward full size {target}")
     buf.destroy()
 
 

@@ -108,12 +108,15 @@ def test_ffn_bwd_rejects_aliased_workspaces():
     buf.destroy()
 
 
-def test_ffn_bwd_full_size_sampled():
+@pytest.mark.parametrize("target", [0.0, 2.0, "adv"])
+def test_ffn_bwd_full_size_sampled(target):
     """Headline shapes: weights drawn on the GPU; the oracle recomputes sampled
-    rows of sampled segments from the home weights (the backward is row-wise)."""
+    rows of sampled segments from the home weights (the backward is row-wise).
+    Balanced, Zipf (maxvio 2) and adversarial routing (one 32768-row segment
+    per rank)."""
     w = synth.WORKLOADS["fwd_r8_s4096_k8_e256"]
-    log("ffn bwd full size")
-    topk, _ = synth.routing(w, 2.0)
+    log(f"ffn bwd full size target={target}")
+    topk, _ = synth.routing(w, target)
     p = oracle.plan(topk, w.E, w.B, w.token_padding)
     home = [torch.empty((w.E, w.H, w.Hp), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
     for i in range(3):
@@ -132,14 +135,15 @@ def test_ffn_bwd_full_size_sampled():
     torch.cuda.synchronize()
     rng = np.random.default_rng(8)
     segs = [(d, row) for d in range(w.R) for row in range(w.E + w.B) if p.seg_tokens[d, row] > 0]
-    pick = [segs[i] for i in rng.choice(len(segs), 5, replace=False)]
+    pick = [segs[i] for i in rng.choice(len(segs), min(5, len(segs)), replace=False)]
     xs = host_bf16(x).reshape(-1, w.H)
     ds = host_bf16(dout).reshape(-1, w.H)
     for d, row in pick:
         e = row if row < w.E else p.prefetch_src[d, row - w.E]
         end = p.cu_seqlens[d, row]
         start = end - p.seg_len[d, row]
-        slots = start + rng.choice(p.seg_tokens[d, row], min(16, p.seg_tokens[d, row]), replace=False)
+        n_pick = min(48 if p.seg_tokens[d, row] > 4096 else 16, p.seg_tokens[d, row])
+        slots = start + rng.choice(p.seg_tokens[d, row], n_pick, replace=False)
         toks = p.src[d, slots] // w.K
         wts = [host_bf16(home[i][e]) for i in range(3)]
         want = oracle.ffn_token_backward(xs[toks], ds[toks], *wts)

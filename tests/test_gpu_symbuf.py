@@ -8,9 +8,11 @@ Weight buffer", "Gradient buffer").
 * prefetch_weight_views fills rows [E,E+B) of each view from rows [0,E) of
   the same view, as the oracle's plan says (prefetch_src), bit for bit;
 * the grouped FFN, forward and backward, over the views (experts located by
-  row index only) is bit-identical to the same call over the symbuf's
-  home/slots ranges and over ordinary device tensors, whose parity with the
-  oracle the FFN tests establish;
+  row index only) matches the oracle's grouped FFN on host-drawn weights
+  (forward and backward tolerances of the FFN tests) and is bit-identical to
+  the same call over the symbuf's home/slots ranges and over ordinary device
+  tensors; at the headline shape sampled rows are checked against the
+  oracle's per-token FFN;
 * an fp32 gradient symbuf takes the weight gradients and reduce_grad through
   its home and slots ranges, bit-identical to ordinary tensors, and its
   per-rank views show the reduce slots."""
@@ -20,7 +22,7 @@ import torch
 
 import moonep_synth as synth
 import oracle
-from gpu_util import buffer_for, dev, dev_bf16, log
+from gpu_util import assert_close_bf16, buffer_for, dev, dev_bf16, host_bf16, log
 
 pytestmark = pytest.mark.gpu
 
@@ -45,10 +47,16 @@ def symbufs(buf, w, n=3, dtype=torch.bfloat16):
     return [SymmetricBuffer(buf, dtype) for _ in range(n)]
 
 
-def filled_weights(buf, w):
+def filled_weights(buf, w, host=None):
+    """Three weight symbufs with the seeded expert weights in their home
+    chunks (drawn on the GPU, or the host arrays `host` copied in) and a
+    sentinel in every slot."""
     sbs = symbufs(buf, w)
     for i, sb in enumerate(sbs):
-        synth.expert_weights_device(w, i, sb.home)
+        if host is None:
+            synth.expert_weights_device(w, i, sb.home)
+        else:
+            sb.home.copy_(dev_bf16(host[i]))
         bits(sb.slots).fill_(0x7F7F)
     return sbs
 
@@ -146,10 +154,12 @@ def test_ffn_views_equal_split_and_plain(name, target):
     w = synth.WORKLOADS[name]
     log(f"ffn views {name} target={target}")
     topk, rw = synth.routing(w, target)
+    x = synth.hidden(w)
+    home_h = [synth.expert_weights_host(w, i) for i in range(3)]
     buf = buffer_for(w)
     plan = buf.plan(dev(topk))
-    x_nvs, _ = buf.dispatch(plan, dev_bf16(synth.hidden(w)), dev(rw))
-    sbs = filled_weights(buf, w)
+    x_nvs, _ = buf.dispatch(plan, dev_bf16(x), dev(rw))
+    sbs = filled_weights(buf, w, home_h)
     views = [sb.views for sb in sbs]
     buf.prefetch_weight_views(plan, views)
     home_plain = [sb.home.clone() for sb in sbs]
@@ -163,6 +173,16 @@ def test_ffn_views_equal_split_and_plain(name, target):
     assert bool((bits(y_views) != 0).any())
     assert same(y_views, y_split)
     assert same(y_views, y_plain)
+    # the views path against the oracle's grouped FFN over the same plan
+    p = oracle.plan(topk, w.E, w.B, w.token_padding)
+    x_nvs_h, _ = oracle.dispatch(p, x)
+    pool_h = [oracle.prefetch_weight(p, home_h[i], np.zeros((w.R, w.B, w.H, w.Hp), np.uint16))
+              for i in range(3)]
+    _, y_want = oracle.expert_ffn(p, x_nvs_h, home_h, pool_h)
+    yv = host_bf16(y_views)
+    for d in range(w.R):
+        end = p.cu_seqlens[d, -1]
+        assert_close_bf16(yv[d, :end], y_want[d, :end], what=f"views y rank {d}")
     # one rank at a time
     y_r = zeros()
     for d in range(w.R):
@@ -177,11 +197,14 @@ def test_ffn_bwd_views_equal_plain():
     w = synth.WORKLOADS["bwd_r8_s1024_k4_e32"]
     log(f"ffn bwd views {w.name}")
     topk, rw = synth.routing(w, 2.0)
+    x = synth.hidden(w)
+    dout = synth.grad_out(w, w.H)
+    home_h = [synth.expert_weights_host(w, i) for i in range(3)]
     buf = buffer_for(w)
     plan = buf.plan(dev(topk))
-    x_nvs, _ = buf.dispatch(plan, dev_bf16(synth.hidden(w)))
-    dy_nvs, _ = buf.dispatch(plan, dev_bf16(synth.grad_out(w, w.H)))
-    sbs = filled_weights(buf, w)
+    x_nvs, _ = buf.dispatch(plan, dev_bf16(x))
+    dy_nvs, _ = buf.dispatch(plan, dev_bf16(dout))
+    sbs = filled_weights(buf, w, home_h)
     views = [sb.views for sb in sbs]
     buf.prefetch_weight_views(plan, views)
     home_plain = [sb.home.clone() for sb in sbs]
@@ -199,6 +222,20 @@ def test_ffn_bwd_views_equal_plain():
     for k, (u, v) in enumerate(zip(a, b)):
         assert bool((bits(u) != 0).any()), k
         assert same(u, v), k
+    # the views path against the oracle's grouped FFN backward
+    p = oracle.plan(topk, w.E, w.B, w.token_padding)
+    x_nvs_h, _ = oracle.dispatch(p, x)
+    dy_nvs_h, _ = oracle.dispatch(p, dout)
+    pool_h = [oracle.prefetch_weight(p, home_h[i], np.zeros((w.R, w.B, w.H, w.Hp), np.uint16))
+              for i in range(3)]
+    ranks = [0, 3, 6]
+    want = oracle.expert_ffn_backward(p, x_nvs_h, dy_nvs_h, home_h, pool_h, ranks=ranks)
+    for nm, g_, w_ in zip(("dz", "dg", "du", "dx"), a, want):
+        gh = host_bf16(g_)
+        for d in ranks:
+            end = p.cu_seqlens[d, -1]
+            assert_close_bf16(gh[d, :end], w_[d, :end], what=f"views {nm} rank {d}",
+                              ulps=1 if nm == "dz" else 2)
     del sbs, views
     buf.destroy()
 
@@ -266,5 +303,27 @@ def test_ffn_views_full_size():
                    y_nvs=y_split)
     torch.cuda.synchronize()
     assert same(y_views, y_split)
+    # sampled rows of every rank's prefetch rows (remote experts read through
+    # the rank's own slots) and of a home row, against the oracle's per-token FFN
+    po = oracle.plan(topk, w.E, w.B, w.token_padding)
+    x_h = synth.hidden(w)
+    xs = x_h.reshape(-1, w.H)
+    rng = np.random.default_rng(12)
+    checked = 0
+    for d in range(w.R):
+        rows = [r for r in range(w.E + w.B) if po.seg_tokens[d, r] > 0]
+        for row in (rows[0], rows[-1]):
+            e = row if row < w.E else po.prefetch_src[d, row - w.E]
+            end = po.cu_seqlens[d, row]
+            start = end - po.seg_len[d, row]
+            slots = start + rng.choice(po.seg_tokens[d, row], min(8, po.seg_tokens[d, row]),
+                                       replace=False)
+            toks = po.src[d, slots] // w.K
+            wts = [host_bf16(sbs[i].views[d, row]) for i in range(3)]
+            assert all(np.array_equal(wt, host_bf16(sbs[i].home[e])) for i, wt in enumerate(wts))
+            _, yw = oracle.ffn_token(xs[toks], *wts)
+            assert_close_bf16(host_bf16(y_views[d, slots]), yw, what=f"views y d={d} row={row}")
+            checked += 1
+    assert checked == 2 * w.R
     del sbs, views
     buf.destroy()
