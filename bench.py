@@ -123,14 +123,76 @@ def measured_traffic(kernel):
     return int(fields[bkey].strip())
 
 
-def cpu_baseline(w, host_routing, main_target, chunk=1024):
-    """The oracle on the host, on a bounded sample of the workload: the full
-    plan of every routing in the sweep, then dispatch and combine of the whole
-    hidden state for the `main_target` routing, in `chunk`-column slices (so
-    the oracle's working set stays near 1 GB)."""
+def _blas_threads():
+    """Threads of the BLAS numpy calls into (threadpoolctl's report)."""
+    try:
+        import threadpoolctl
+        n = [i["num_threads"] for i in threadpoolctl.threadpool_info() if i["user_api"] == "blas"]
+        return int(n[0]) if n else None
+    except Exception:
+        return None
+
+
+def cpu_ffn_leg(w, p, x_dev, home_dev, budget_s=15.0, max_segments=16):
+    """The oracle's per-token SwiGLU (oracle.ffn_token, float64 BLAS on every
+    core the process may use) over a bounded sample of the FFN: the segments
+    of rank 0 in row order, each with its real tokens and its expert's home
+    weights copied from the GPU, until `max_segments` or `budget_s` seconds of
+    oracle time.  Returns the oracle's TFLOP/s over the sample (6 H H' flop
+    per token, as the GPU figure counts) and the whole job's time at that
+    rate."""
     import oracle
-    os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")
-    x = synth.hidden(w)
+    import torch
+    cores = len(os.sched_getaffinity(0))
+    try:
+        import threadpoolctl
+        limit = threadpoolctl.threadpool_limits(limits=cores, user_api="blas")
+    except Exception:
+        limit = None
+    rows = [row for row in range(w.E + w.B) if p.seg_tokens[0, row] > 0]
+    t_ffn, flops, toks, nseg = 0.0, 0.0, 0, 0
+    xf = x_dev.reshape(-1, w.H)
+    for row in rows[:max_segments]:
+        e = row if row < w.E else int(p.prefetch_src[0, row - w.E])
+        n = int(p.seg_tokens[0, row])
+        start = int(p.cu_seqlens[0, row] - p.seg_len[0, row])
+        tok = p.src[0, start:start + n] // w.K
+        xs = xf[torch.from_numpy(tok.astype(np.int64)).to(x_dev.device)].cpu().view(
+            torch.int16).numpy().view(np.uint16)
+        wts = [home_dev[i][e].cpu().view(torch.int16).numpy().view(np.uint16) for i in range(3)]
+        t0 = time.perf_counter()
+        oracle.ffn_token(xs, *wts)
+        t_ffn += time.perf_counter() - t0
+        flops += 6.0 * w.H * w.Hp * n
+        toks += n
+        nseg += 1
+        if t_ffn > budget_s:
+            break
+    threads = _blas_threads()
+    if limit is not None:
+        limit.restore_original_limits()
+    rate = flops / t_ffn
+    return {"value": round(rate / 1e12, 5), "unit": "TFLOP/s", "cores": threads or cores,
+            "kind": "oracle",
+            "sample": f"oracle.ffn_token (float64 BLAS) over the first {nseg} segments of rank 0 "
+                      f"({toks} real tokens) at the baseline's routing, weights and tokens "
+                      f"copied from the GPU; the whole job ({w.R} ranks x S*K slots) would take "
+                      f"{ffn_flops(w) / rate:.1f} s at this rate",
+            "seconds": round(t_ffn, 3), "flops": flops}
+
+
+def cpu_baseline(w, host_routing, main_target, x_dev, home_dev, chunk=1024):
+    """The oracle on the host, on a bounded sample of the workload.
+
+    Plan + dispatch + combine (the GB/s half of the metric, numpy fancy
+    indexing on one thread): the full plan of every routing in the sweep,
+    then dispatch and combine of the whole hidden state for the `main_target`
+    routing, in `chunk`-column slices (so the oracle's working set stays near
+    1 GB).  Grouped FFN (the TFLOP/s half): cpu_ffn_leg on the same routing.
+    The host's core count and the process's usable cores are stated."""
+    import oracle
+    import torch
+    x = x_dev.cpu().view(torch.int16).numpy().view(np.uint16)
     t_plan = 0.0
     plans = {}
     for t, (topk, rw) in host_routing.items():
@@ -154,17 +216,21 @@ def cpu_baseline(w, host_routing, main_target, chunk=1024):
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"plan of all {len(plans)} {w.name} routings of the sweep + dispatch and "
                       f"combine of the full hidden state at maxvio {main_target} ({chunk}-column "
-                      f"slices); numpy, one thread",
+                      f"slices); numpy fancy indexing and fp32 sums, single-threaded",
             "seconds": {"plan": round(t_plan, 3), "dispatch": round(t_disp, 3),
-                        "combine": round(t_comb, 3), "total": round(total, 3)}}
+                        "combine": round(t_comb, 3), "total": round(total, 3)},
+            "host_cores": os.cpu_count(), "usable_cores": len(os.sched_getaffinity(0)),
+            "ffn": cpu_ffn_leg(w, p, x_dev, home_dev)}
 
 
-def time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool, steps, warmup):
+def time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool, steps, warmup, flush):
     """Backward of the step, timed per stage with HIP events on the launch
     stream.  For each batch the forward inputs of the backward (plan, x_nvs,
-    prefetched weights, Z) are recomputed untimed; then: combine bwd (dispatch
-    of dOut), FFN backward (dZ, dG/dU, dX), dispatch bwd (unweighted combine
-    of dX), dW for gate, up and down, and reduce_grad."""
+    prefetched weights, Z) are recomputed untimed, then the cache is flushed;
+    then: combine bwd (dispatch of dOut), FFN backward (dZ, dG/dU, dX),
+    dispatch bwd (unweighted combine of dX), dW for gate, up and down, and
+    reduce_grad.  Stage times are medians per maxvio target; the weight
+    gradients are also set against both of their bounds (MFMA and HBM)."""
     import torch
     dev = x_nvs.device
     g = torch.Generator(device=dev).manual_seed(1)
@@ -179,13 +245,15 @@ def time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool, steps, warmup)
     names = ["combine_bwd", "ffn_bwd", "dispatch_bwd", "wgrad_x3", "reduce_grad"]
     per = {n: [] for n in names}
     wgrad_bytes = []
+    used = []
     EB = w.E + w.B
     for i in range(warmup + steps):
-        _, topk, _ = batches[i % len(batches)]
+        t, topk, _ = batches[i % len(batches)]
         buf.plan(topk, plan=plan)
         buf.dispatch(plan, x, x_nvs=x_nvs)
         buf.prefetch_weight(plan, home, pool)
         buf.expert_gateup(plan, x_nvs, home, pool, z_ws)
+        flush()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         ev[0].record()
         buf.dispatch(plan, dout, x_nvs=dy_nvs)
@@ -202,6 +270,7 @@ def time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool, steps, warmup)
         ev[5].record()
         torch.cuda.synchronize()
         if i >= warmup:
+            used.append(t)
             for j, n in enumerate(names):
                 per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
             # each used (rank, weight row) pair's fp32 gradient rows are read and
@@ -218,11 +287,29 @@ def time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool, steps, warmup)
     out["ffn_bwd_TFLOPs"] = round(10 * hh * slots / mean["ffn_bwd"] / 1e12, 1)
     out["wgrad_TFLOPs"] = round(6 * hh * slots / mean["wgrad_x3"] / 1e12, 1)
     out["wgrad_GBps"] = round(sum(wgrad_bytes) / sum(per["wgrad_x3"]) / 1e9, 1)
+    # the three weight-gradient launches against both bounds: the MFMA time of
+    # their flops and the HBM time of their algorithmic bytes at the published
+    # peaks; the binding one is the larger
+    wb = float(np.mean(wgrad_bytes))
+    t_mfma = 6 * hh * slots / (BF16_PEAK_TFLOPS * 1e12)
+    t_hbm = wb / (HBM_PEAK_GBS * 1e9)
+    out["roofline_wgrad"] = {
+        "kernel": "wgrad_kernel x3 (dWg, dWu, dWd; all ranks)",
+        "bound": "hbm" if t_hbm > t_mfma else "mfma",
+        "mfma_floor_ms": round(t_mfma * 1e3, 3), "hbm_floor_ms": round(t_hbm * 1e3, 3),
+        "measured_ms": round(mean["wgrad_x3"] * 1e3, 3),
+        "frac": round(max(t_mfma, t_hbm) / mean["wgrad_x3"], 4),
+        "frac_of_bf16_peak": round(t_mfma / mean["wgrad_x3"], 4),
+        "algorithmic_bytes": wb, "flops": 6 * hh * slots}
     pb, db, cb = alg_bytes(w)
     out["combine_bwd_GBps"] = round(db / mean["combine_bwd"] / 1e9, 1)
     out["dispatch_bwd_GBps"] = round((slots * 2 * w.H + w.R * w.S * 2 * w.H + 4 * slots)
                                      / mean["dispatch_bwd"] / 1e9, 1)
     out["backward_ms"] = round(sum(mean.values()) * 1e3, 3)
+    out["per_target_median_ms"] = {
+        str(t): {n: round(float(np.median([per[n][i] for i, u in enumerate(used) if u == t]))
+                          * 1e3, 3) for n in names}
+        for t in dict.fromkeys(used)}
     out["note"] = ("flops per real slot: FFN backward 10 H H' (dZ 2, recomputed gate/up 4, "
                    "dX 4), weight gradients 6 H H'; weight-gradient bytes: fp32 read-modify-"
                    "write of each used (rank, weight row) pair's gradient per projection plus "
@@ -493,6 +580,14 @@ def main():
                     help="also time prefetch and the FFN over per-rank [E+B] views on virtual "
                          "memory (SymmetricBuffer) beside ordinary home/pool tensors; needs "
                          "~45 GB more HBM at the headline shape")
+    ap.add_argument("--flush-mb", type=int, default=1024, metavar="MIB",
+                    help="before every timed step, write a scratch buffer of MIB MiB so "
+                         "that the 256 MB last-level cache (MALL) holds nothing of the "
+                         "step's inputs (0: no flush)")
+    ap.add_argument("--sweep-reps", type=int, default=20,
+                    help="per maxvio target: timed repetitions (after 3 warm-up ones) of "
+                         "the step, each after a cache flush; the per-target table reports "
+                         "their medians")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before warmup, run torch.neg over a float32 buffer of MIB MiB "
                          "three times: a plain kernel of known traffic (reads and writes "
@@ -565,8 +660,16 @@ def main():
         del a, b
         print(f"[bench] copy probe: 3 x neg over {args.copy_probe} MiB", file=sys.stderr, flush=True)
 
+    scratch_flush = (torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev)
+                     if args.flush_mb > 0 else None)
+
+    def flush():
+        if scratch_flush is not None:
+            scratch_flush.fill_(1)
+
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
+        flush()
         step(i)
     torch.cuda.synchronize()
 
@@ -585,6 +688,7 @@ def main():
     t0 = time.perf_counter()
     used = []
     for i in range(args.steps):
+        flush()
         used.append(step(i, events[i]))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -605,12 +709,29 @@ def main():
     t_disp = float(np.mean(per["dispatch"]))
     t_comb = float(np.mean(per["combine"]))
 
+    # per-target sweep: 3 warm-up and sweep_reps timed steps at each target,
+    # each after a cache flush; stage medians
+    print(f"[bench] sweep: {args.sweep_reps} steps per target", file=sys.stderr, flush=True)
+    sw = {}
+    for ti, t in enumerate(targets):
+        for _ in range(3):
+            flush()
+            step(ti)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)]
+               for _ in range(args.sweep_reps)]
+        for r in range(args.sweep_reps):
+            flush()
+            step(ti, evs[r])
+        torch.cuda.synchronize()
+        sw[t] = {n: [ev[j].elapsed_time(ev[j + 1]) * 1e-3 for ev in evs]
+                 for j, n in enumerate(names)}
+        sw[t]["ffn"] = [a + b for a, b in zip(sw[t]["gateup"], sw[t]["down"])]
+
     sweep = {}
     for t in targets:
-        idx = [i for i, u in enumerate(used) if u == t]
-        if not idx:
+        if args.sweep_reps <= 0:
             continue
-        m = lambda n: float(np.mean([per[n][i] for i in idx]))
+        m = lambda n: float(np.median(sw[t][n]))
         sweep[str(t)] = {
             "realized_maxvio": round(stats[t]["maxvio"], 4), "dups": stats[t]["dups"],
             "pad_rows": stats[t]["pad_rows"],
@@ -710,12 +831,18 @@ def main():
 
     if args.train:
         result["train"] = time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool,
-                                        args.steps, args.warmup)
+                                        args.steps, args.warmup, flush)
     buf.destroy()
+    scratch_flush = None
+    result["timing"] = (f"stage times from HIP events on the launch stream; {args.flush_mb} MiB "
+                        f"written before every timed step (outside the stage events, inside "
+                        f"ms_per_step) so the last-level cache holds none of the step's inputs; "
+                        f"value and roofline: mean over the {args.steps} timed steps; sweep: "
+                        f"medians of {args.sweep_reps} steps per target")
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         t1 = 1.0 if 1.0 in host_routing else targets[0]
-        result["cpu_baseline"] = cpu_baseline(w, host_routing, t1)
+        result["cpu_baseline"] = cpu_baseline(w, host_routing, t1, x, home)
     print(json.dumps(result), flush=True)
 
 
