@@ -53,84 +53,96 @@ struct DispatchArgs {
   const int32_t* cu;     // [R][E+B]
   const int32_t* segn;   // [R][E+B]
   const int32_t* act;    // [R][2L]
-  int ntok, K, nv, EB, L2, tp, pad_parts, npad_blocks, npad_used, NvS;
-  int xcd_local;          // 1: the grid has one item per wave, a token's waves on one XCD
+  int ntok, K, nv, EB, L2, tp, pad_parts, npad_used, NvS;
+  int item_blocks;        // token workgroups (the padding workgroups follow them)
+  int xcd_local;          // 1: one item per wave, a token's waves on one XCD; 0: a capped grid
 };
 
-// Blocks [0, npad_blocks): zero the padding rows of one active row (one part
-// of it).  Blocks past that: one wave per (token, k) pair and column chunk of
-// 64 kDispVecs vectors (the whole row up to 8192 columns), on a grid of one
-// item per wave: the wave reads the chunk of the token's row and writes it to
-// the pair's slot.  The workgroups of a token run on one XCD, so its K waves
-// take the row from that XCD's L2 (HBM reads 0.96 -> 0.48 GB at the headline,
-// 1% faster).  One write per wave on a large grid measured 10-14% faster in
-// the kernel than one wave writing all K slots of its tokens in a
-// grid-stride loop; smaller chunks (7 or 4 vectors) were 15-50% slower.
+// Padding item pb: zero the padding rows (and their route weights) of one
+// part of one active row.
+__device__ __forceinline__ void dispatch_pad(const DispatchArgs& a, int pb, int wv, int lane) {
+  const int part = pb % a.pad_parts;
+  const int dq = pb / a.pad_parts;        // d * 2L + q
+  const int row = a.act[dq];
+  if (row < 0) return;
+  const int d = dq / a.L2;
+  const int end = a.cu[d * a.EB + row];
+  const int n = a.segn[d * a.EB + row];
+  const int len = round_up(n, a.tp);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int i = end - len + n + part * kWaves + wv; i < end; i += a.pad_parts * kWaves) {
+    const int64_t slot = (int64_t)d * a.NvS + i;
+    u32x4* dst = a.x_nvs + slot * a.nv;
+    for (int v = lane; v < a.nv; v += 64) __builtin_nontemporal_store(zero, dst + v);
+    if (a.rw_nvs && lane == 0) a.rw_nvs[slot] = 0.0f;
+  }
+}
+
+// Token item `it` = ((token, k) pair, column chunk of 64 kDispVecs vectors):
+// the wave reads the chunk of the token's row and writes it to the pair's
+// slot (and the pair's route weight).
+__device__ __forceinline__ void dispatch_item(const DispatchArgs& a, int64_t it, int nch,
+                                              int lane) {
+  const int64_t p = it / nch;                           // (token, k) pair
+  const int c0 = uniform((int)(it - p * nch)) * 64 * kDispVecs;
+  const int tok = uniform((int)(p / a.K));
+  const int slot = uniform(a.dest[p]);
+  const u32x4* src = a.x + (int64_t)tok * a.nv;
+  u32x4* dst = a.x_nvs + (int64_t)slot * a.nv;
+  u32x4 buf[kDispVecs];
+#pragma unroll
+  for (int u = 0; u < kDispVecs; ++u) {
+    const int v = c0 + u * 64 + lane;
+    if (v < a.nv) buf[u] = src[v];
+  }
+#pragma unroll
+  for (int u = 0; u < kDispVecs; ++u) {
+    const int v = c0 + u * 64 + lane;
+    if (v < a.nv) dst[v] = buf[u];            // non-temporal stores measured 15% slower
+  }
+  if (a.rw && c0 == 0 && lane == 0) a.rw_nvs[slot] = a.rw[p];
+}
+
+// Without a CU budget the grid has one piece of work per workgroup: the
+// token items, one per wave, then the padding items (one part of one active
+// row's padding per workgroup; launched first instead they measured the same
+// within noise).  A token item is a (token, k) pair and a column chunk of 64
+// kDispVecs vectors (the whole row up to 8192 columns).  The workgroups of a
+// token run on one XCD, so its K waves take the row from that XCD's L2 (HBM
+// reads 0.96 -> 0.48 GB at the headline, 1% faster).  One write per wave on a
+// large grid measured 10-14% faster in the kernel than one wave writing all
+// K slots of its tokens in a grid-stride loop; smaller chunks (7 or 4
+// vectors) were 15-50% slower.  With a CU budget (num_cus) the grid is capped
+// and every workgroup loops over the padding items, then over the token
+// items.
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  if ((int)blockIdx.x < a.npad_blocks) {
-    if ((int)blockIdx.x >= a.npad_used) return;        // rounding of the padding blocks
-    const int part = blockIdx.x % a.pad_parts;
-    const int dq = blockIdx.x / a.pad_parts;        // d * 2L + q
-    const int row = a.act[dq];
-    if (row < 0) return;
-    const int d = dq / a.L2;
-    const int end = a.cu[d * a.EB + row];
-    const int n = a.segn[d * a.EB + row];
-    const int len = round_up(n, a.tp);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int i = end - len + n + part * kWaves + wv; i < end; i += a.pad_parts * kWaves) {
-      const int64_t slot = (int64_t)d * a.NvS + i;
-      u32x4* dst = a.x_nvs + slot * a.nv;
-      for (int v = lane; v < a.nv; v += 64) __builtin_nontemporal_store(zero, dst + v);
-      if (a.rw_nvs && lane == 0) a.rw_nvs[slot] = 0.0f;
-    }
-    return;
-  }
-  const int nblk = gridDim.x - a.npad_blocks;
   const int nch = (a.nv + 64 * kDispVecs - 1) / (64 * kDispVecs);   // column chunks per row
   const int per_tok = a.K * nch;                          // items of a token
-  int64_t it, step, items;
   if (a.xcd_local) {
+    // token workgroups first, the padding workgroups after them (they fill
+    // the tail of the token waves)
+    const int b = (int)blockIdx.x;
+    if (b >= a.item_blocks) {
+      if (b - a.item_blocks < a.npad_used) dispatch_pad(a, b - a.item_blocks, wv, lane);
+      return;
+    }
     // the wpt workgroups of token t are t's group of 8 tokens x wpt, at the
-    // position of t in its group: all on XCD t mod 8 (npad_blocks is a
-    // multiple of 8), so the K reads of its row share that XCD's L2
+    // position of t in its group: all on XCD t mod 8, so the K reads of its
+    // row share that XCD's L2
     const int wpt = (per_tok + kWaves - 1) / kWaves;
-    const int b = (int)blockIdx.x - a.npad_blocks;
     const int c = b / kXcdsMove;
     const int tok = (c / wpt) * kXcdsMove + b % kXcdsMove;
     const int item = (c % wpt) * kWaves + wv;
     if (tok >= a.ntok || item >= per_tok) return;
-    it = (int64_t)tok * per_tok + item;
-    step = 0;
-    items = it + 1;
-  } else {
-    it = ((int64_t)blockIdx.x - a.npad_blocks) * kWaves + wv;
-    step = (int64_t)nblk * kWaves;
-    items = (int64_t)a.ntok * per_tok;
+    dispatch_item(a, (int64_t)tok * per_tok + item, nch, lane);
+    return;
   }
-  for (; it < items; it += step) {
-    const int64_t p = it / nch;                           // (token, k) pair
-    const int c0 = uniform((int)(it - p * nch)) * 64 * kDispVecs;
-    const int tok = uniform((int)(p / a.K));
-    const int slot = uniform(a.dest[p]);
-    const u32x4* src = a.x + (int64_t)tok * a.nv;
-    u32x4* dst = a.x_nvs + (int64_t)slot * a.nv;
-    u32x4 buf[kDispVecs];
-#pragma unroll
-    for (int u = 0; u < kDispVecs; ++u) {
-      const int v = c0 + u * 64 + lane;
-      if (v < a.nv) buf[u] = src[v];
-    }
-#pragma unroll
-    for (int u = 0; u < kDispVecs; ++u) {
-      const int v = c0 + u * 64 + lane;
-      if (v < a.nv) dst[v] = buf[u];
-    }
-    if (a.rw && c0 == 0 && lane == 0) a.rw_nvs[slot] = a.rw[p];
-    if (step == 0) break;
-  }
+  for (int pb = blockIdx.x; pb < a.npad_used; pb += gridDim.x) dispatch_pad(a, pb, wv, lane);
+  const int64_t items = (int64_t)a.ntok * per_tok;
+  for (int64_t it = (int64_t)blockIdx.x * kWaves + wv; it < items; it += (int64_t)gridDim.x * kWaves)
+    dispatch_item(a, it, nch, lane);
 }
 
 struct CombineArgs {
@@ -351,13 +363,19 @@ hipError_t launch_dispatch(const Ctx& c, const moonep_plan_t& p, const uint16_t*
   a.tp = d.tp; a.NvS = (int)d.NvS;
   a.pad_parts = (d.tp + 4 * kWaves - 1) / (4 * kWaves);
   a.npad_used = d.R * a.L2 * a.pad_parts;
-  a.npad_blocks = (a.npad_used + kXcdsMove - 1) / kXcdsMove * kXcdsMove;
   const int nch = (a.nv + 64 * kDispVecs - 1) / (64 * kDispVecs);
   const int64_t wpt = ((int64_t)a.K * nch + kWaves - 1) / kWaves;
   const int64_t want = (a.ntok + kXcdsMove - 1) / kXcdsMove * kXcdsMove * wpt;
-  const int item_blocks = capped_grid(c, want);
-  a.xcd_local = item_blocks == want ? 1 : 0;     // a CU budget falls back to a grid-stride loop
-  dispatch_kernel<<<a.npad_blocks + item_blocks, kThreads, 0, s>>>(a);
+  if (d.num_cus > 0) {
+    // a CU budget: the whole grid (padding and token items) within it
+    a.xcd_local = 0;
+    a.item_blocks = 0;
+    dispatch_kernel<<<capped_grid(c, a.npad_used + want), kThreads, 0, s>>>(a);
+  } else {
+    a.xcd_local = 1;
+    a.item_blocks = (int)want;
+    dispatch_kernel<<<(unsigned)(want + a.npad_used), kThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -58,8 +58,12 @@ def test_dispatch_ragged_widths(width):
     run(synth.WORKLOADS["tiny_r4_s64_k2_e8"], "adv", width=width)
 
 
-def test_dispatch_cu_budget():
-    run(synth.WORKLOADS["mid_r8_s1024_k4_e32"], 1.0, num_cus=4)
+@pytest.mark.parametrize("name,num_cus", [("mid_r8_s1024_k4_e32", 4), ("tiny_r4_s64_k2_e8", 1)])
+def test_dispatch_cu_budget(name, num_cus):
+    """A CU budget caps the whole dispatch grid (num_cus * 8 workgroups, here
+    down to 8): every workgroup loops over the padding items, then over the
+    token items."""
+    run(synth.WORKLOADS[name], 1.0, num_cus=num_cus)
 
 
 @pytest.mark.parametrize("name,target", [("fwd_r8_s4096_k8_e256", 2.0),
