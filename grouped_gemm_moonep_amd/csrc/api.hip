@@ -185,7 +185,6 @@ moonep_status_t moonep_create(const moonep_config_t* cfg, moonep_handle_t* out) 
   }
   struct { int32_t** p; int64_t n; } allocs[] = {
       {&c.cc, (int64_t)d.R * d.nch * d.E},
-      {&c.rankpre, (int64_t)d.R * d.E},
       {&c.shift, (int64_t)d.R * d.E},
       {&c.pieces, (int64_t)d.R * (d.R + 1) * 2},
       {&c.npieces, d.R},
@@ -205,7 +204,7 @@ moonep_status_t moonep_create(const moonep_config_t* cfg, moonep_handle_t* out) 
 moonep_status_t moonep_destroy(moonep_handle_t h) {
   if (!h) return MOONEP_OK;
   Ctx& c = h->c;
-  int32_t* ptrs[] = {c.cc, c.rankpre, c.shift, c.pieces, c.npieces, c.line,
+  int32_t* ptrs[] = {c.cc, c.shift, c.pieces, c.npieces, c.line,
                      c.chunk_err};
   hipError_t err = hipSuccess;
   for (int32_t* p : ptrs)

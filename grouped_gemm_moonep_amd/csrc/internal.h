@@ -47,7 +47,6 @@ struct Ctx {
   int num_cu_device;
   // planning scratch (device)
   int32_t* cc;        // [R][nch][E] chunk counts, then line-position bases
-  int32_t* rankpre;   // [R][E] sum of counts of lower ranks
   int32_t* shift;     // [R][E] slot - line position for (d, e)
   int32_t* pieces;    // [R groups][R+1][2] (hi, rank) of each line piece
   int32_t* npieces;   // [R]

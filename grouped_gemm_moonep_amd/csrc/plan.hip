@@ -45,7 +45,6 @@ struct PlanArgs {
   const int32_t* tpe;
   int32_t* cc;
   int32_t* chunk_err;
-  int32_t* rankpre;
   int32_t* shift;
   int32_t* pieces;
   int32_t* npieces;
@@ -100,30 +99,54 @@ __global__ __launch_bounds__(kPlanChunk) void plan_hist(PlanArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Block-wide exclusive scan of v over all kSolveThreads threads.
-__device__ int block_exclusive_scan(int v, int* total, int* scratch /*[32]*/) {
+// Block-wide exclusive scan of two values at once over all kSolveThreads
+// threads (16 waves): a shuffle scan within each wave, then wave 0 scans the
+// 16 wave totals with shuffles.  Two barriers.  scratch holds 64 ints; its
+// halves are written and read on either side of the first barrier of the
+// next call, so back-to-back calls need no barrier in between.
+constexpr int kSolveWaves = kSolveThreads / 64;
+__device__ __forceinline__ void block_scan2(int x, int y, int* ex, int* ey, int* tx, int* ty,
+                                            int* scratch /*[64]*/) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int x = v;
+  int ix = x, iy = y;
   for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) scratch[wv] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < kSolveThreads / 64; ++i) {
-      const int t = scratch[i];
-      scratch[i] = run;
-      run += t;
+    const int ax = __shfl_up(ix, o, 64), ay = __shfl_up(iy, o, 64);
+    if (lane >= o) {
+      ix += ax;
+      iy += ay;
     }
-    scratch[16] = run;
+  }
+  if (lane == 63) {
+    scratch[wv] = ix;
+    scratch[kSolveWaves + wv] = iy;
   }
   __syncthreads();
-  const int res = x - v + scratch[wv];
-  *total = scratch[16];
+  if (wv == 0) {
+    int sx = lane < kSolveWaves ? scratch[lane] : 0;
+    int sy = lane < kSolveWaves ? scratch[kSolveWaves + lane] : 0;
+    for (int o = 1; o < kSolveWaves; o <<= 1) {
+      const int ax = __shfl_up(sx, o, 64), ay = __shfl_up(sy, o, 64);
+      if (lane >= o) {
+        sx += ax;
+        sy += ay;
+      }
+    }
+    if (lane < kSolveWaves) {
+      scratch[2 * kSolveWaves + lane] = sx;        // inclusive prefixes of the wave totals
+      scratch[3 * kSolveWaves + lane] = sy;
+    }
+  }
   __syncthreads();
-  return res;
+  *ex = (wv ? scratch[2 * kSolveWaves + wv - 1] : 0) + ix - x;
+  *ey = (wv ? scratch[3 * kSolveWaves + wv - 1] : 0) + iy - y;
+  *tx = scratch[3 * kSolveWaves - 1];
+  *ty = scratch[4 * kSolveWaves - 1];
+}
+
+// Wave-wide sum (all 64 lanes get it).
+__device__ __forceinline__ int wave_sum(int v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -131,69 +154,72 @@ __device__ int block_exclusive_scan(int v, int* total, int* scratch /*[32]*/) {
 __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   __shared__ int T[kMaxE];
   __shared__ int aline[kMaxE];
-  __shared__ int W[kMaxR], keep[kMaxR], X[kMaxR], D[kMaxR], need[kMaxR];
+  __shared__ int W[kMaxR], keep[kMaxR], X[kMaxR], need[kMaxR];
   __shared__ int donors[kMaxR], queue[2 * kMaxR + 2];
-  __shared__ int don_g[kMaxR + 1], don_r[kMaxR + 1], don_amt[kMaxR + 1], don_lo[kMaxR + 1];
+  __shared__ int don_g[kMaxR + 1], don_r[kMaxR + 1], don_amt[kMaxR + 1];
   __shared__ int recv_g[kMaxR], recv_lo[kMaxR], recv_hi[kMaxR];
   __shared__ int ent_n[2 * kMaxE], ent_lo[2 * kMaxE], ent_row[2 * kMaxE];
   __shared__ int act_row[2 * kMaxE], act_end[2 * kMaxE], act_n[2 * kMaxE];
-  __shared__ int nact[kMaxR], nrem[kMaxR], npf[kMaxR];
+  __shared__ int nact[kMaxR], nrem[kMaxR], npf[kMaxR], pfpre[kMaxR];
   __shared__ int hcount[kMaxE];
   __shared__ int ord_len[3 * kMaxE], ord_ent[3 * kMaxE], ord_cnt[3 * kMaxE];  // phase F
-  __shared__ int scan_scratch[32];
-  __shared__ int s_err, s_maxload, s_ndon, s_dups, s_pad;
+  __shared__ int scan_scratch[4 * kSolveWaves];
+  __shared__ int s_err, s_maxload, s_ndon, s_dups, s_pad, s_nd, s_nq;
 
   const int tid = threadIdx.x;
   const int R = a.R, E = a.E, L = a.L, B = a.B, nch = a.nch;
   const int C = a.S * a.K;
   const int RE = R * E;
   if (tid == 0) {
-    s_err = 0; s_maxload = 0; s_ndon = 0; s_dups = 0; s_pad = 0;
+    s_err = 0; s_maxload = 0; s_ndon = 0; s_dups = 0; s_pad = 0; s_nd = 0; s_nq = 0;
   }
+  for (int e = tid; e < E; e += kSolveThreads) T[e] = 0;
+  for (int g = tid; g < R; g += kSolveThreads) W[g] = 0;
   __syncthreads();
 
-  // Phase A: counts per (r, e) and exclusive per-chunk prefix (in place).
-  // Loads are batched 16 at a time so each thread keeps 16 in flight.
-  for (int idx = tid; idx < RE; idx += kSolveThreads) {
-    const int r = idx / E, e = idx - (idx / E) * E;
-    int32_t* col = a.cc + (int64_t)r * nch * E + e;
-    int run = 0;
-    for (int ch0 = 0; ch0 < nch; ch0 += 16) {
-      int v[16];
+  // Phase A: counts per (r, e), the exclusive per-chunk prefix (in place) and
+  // the expert loads T_e (an order-independent integer sum in LDS).  Two
+  // (r, e) columns per pass with all their chunk loads in flight together,
+  // and the per-chunk error bits loaded beside them.
+  {
+    constexpr int kBatch = 8;            // chunk loads per column in flight
+    int cerr = 0;
+    for (int i = tid; i < R * nch; i += kSolveThreads) cerr |= a.chunk_err[i];
+    for (int i0 = tid; i0 < RE; i0 += 2 * kSolveThreads) {
+      const int i1 = i0 + kSolveThreads;
+      const bool has1 = i1 < RE;
+      int32_t* col0 = a.cc + (int64_t)(i0 / E) * nch * E + (i0 % E);
+      int32_t* col1 = has1 ? a.cc + (int64_t)(i1 / E) * nch * E + (i1 % E) : col0;
+      int run0 = 0, run1 = 0;
+      for (int ch0 = 0; ch0 < nch; ch0 += kBatch) {
+        int v0[kBatch], v1[kBatch];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = ch0 + u < nch ? col[(int64_t)(ch0 + u) * E] : 0;
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (ch0 + u < nch) {
-          col[(int64_t)(ch0 + u) * E] = run;
-          run += v[u];
+        for (int u = 0; u < kBatch; ++u) {
+          const bool ok = ch0 + u < nch;
+          v0[u] = ok ? col0[(int64_t)(ch0 + u) * E] : 0;
+          v1[u] = ok && has1 ? col1[(int64_t)(ch0 + u) * E] : 0;
         }
-    }
-    a.counts[idx] = run;
-    if (a.tpe && a.tpe[idx] != run) atomicOr(&s_err, MOONEP_ROUTE_COUNTS);
-  }
-  for (int i = tid; i < R * nch; i += kSolveThreads) {
-    const int v = a.chunk_err[i];
-    if (v) atomicOr(&s_err, v);
-  }
-  __syncthreads();
-
-  // Phase B: expert loads T_e and the exclusive prefix over ranks.
-  for (int e = tid; e < E; e += kSolveThreads) {
-    int run = 0;
-    for (int r0 = 0; r0 < R; r0 += 8) {
-      int v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = r0 + u < R ? a.counts[(r0 + u) * E + e] : 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (r0 + u < R) {
-          a.rankpre[(r0 + u) * E + e] = run;
-          run += v[u];
-        }
+        for (int u = 0; u < kBatch; ++u)
+          if (ch0 + u < nch) {
+            col0[(int64_t)(ch0 + u) * E] = run0;
+            run0 += v0[u];
+            if (has1) {
+              col1[(int64_t)(ch0 + u) * E] = run1;
+              run1 += v1[u];
+            }
+          }
+      }
+      a.counts[i0] = run0;
+      atomicAdd(&T[i0 % E], run0);
+      if (a.tpe && a.tpe[i0] != run0) cerr |= MOONEP_ROUTE_COUNTS;
+      if (has1) {
+        a.counts[i1] = run1;
+        atomicAdd(&T[i1 % E], run1);
+        if (a.tpe && a.tpe[i1] != run1) cerr |= MOONEP_ROUTE_COUNTS;
+      }
     }
-    T[e] = run;
-    atomicMax(&s_maxload, run);
+    if (cerr) atomicOr(&s_err, cerr);
   }
   __syncthreads();
   const int err = s_err;
@@ -217,61 +243,57 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     return;
   }
 
-  // Phase C: line start of every expert (experts of a group by (T, id)),
-  // group loads.
+  // Phase C: line start of every expert (experts of a group by (T, id)), the
+  // group loads W_g and the largest load.
   for (int e = tid; e < E; e += kSolveThreads) {
     const int g = e / L;
     const int te = T[e];
     int acc = 0;
+#pragma unroll 8
     for (int f = g * L; f < (g + 1) * L; ++f) {
       const int tf = T[f];
-      if (tf < te || (tf == te && f < e)) acc += tf;
+      acc += (tf < te || (tf == te && f < e)) ? tf : 0;
     }
     aline[e] = acc;
     a.line[e] = acc;
-  }
-  for (int g = tid; g < R; g += kSolveThreads) {
-    int w = 0;
-    for (int f = g * L; f < (g + 1) * L; ++f) w += T[f];
-    W[g] = w;
+    atomicAdd(&W[g], te);
+    atomicMax(&s_maxload, te);
   }
   __syncthreads();
 
-  // Phase D: keep/excess/deficit per group, donors ordered by (-X, g) and
-  // receivers by (-D, r) (each group finds its own position), then the
-  // chain-greedy itself (one thread, at most 2R steps), then the line pieces
-  // of every group (one thread per group).
+  // Phase D: keep/excess/deficit per group; each group finds its position
+  // among the donors (by (-X, g)) and the receivers (by (-D, r)) from the
+  // group loads directly; then the chain-greedy itself (one thread, at most
+  // 2R steps); then the line pieces of every group (one thread per group).
   for (int g = tid; g < R; g += kSolveThreads) {
-    keep[g] = W[g] < C ? W[g] : C;
-    X[g] = W[g] - keep[g];
-    D[g] = C - keep[g];
-    need[g] = D[g];
+    const int wg = W[g];
+    const int xg = wg > C ? wg - C : 0, dg = wg < C ? C - wg : 0;
+    keep[g] = wg < C ? wg : C;
+    X[g] = xg;
+    need[g] = dg;
     recv_g[g] = -1;
     recv_lo[g] = 0;
     recv_hi[g] = 0;
-  }
-  __syncthreads();
-  for (int g = tid; g < R; g += kSolveThreads) {
-    int pos = 0;
-    if (X[g] > 0) {
-      for (int h = 0; h < R; ++h)
-        if (X[h] > 0 && (X[h] > X[g] || (X[h] == X[g] && h < g))) ++pos;
-      donors[pos] = g;
+    int pd = 0, pr = 0;
+    for (int h = 0; h < R; ++h) {
+      const int wh = W[h];
+      const int xh = wh > C ? wh - C : 0, dh = wh < C ? C - wh : 0;
+      pd += xh > 0 && (xh > xg || (xh == xg && h < g));
+      pr += dh > 0 && (dh > dg || (dh == dg && h < g));
     }
-    if (D[g] > 0) {
-      pos = 0;
-      for (int h = 0; h < R; ++h)
-        if (D[h] > 0 && (D[h] > D[g] || (D[h] == D[g] && h < g))) ++pos;
-      queue[pos] = g;
+    if (xg > 0) {
+      donors[pd] = g;
+      atomicAdd(&s_nd, 1);
+    }
+    if (dg > 0) {
+      queue[pr] = g;
+      atomicAdd(&s_nq, 1);
     }
   }
   __syncthreads();
   if (tid == 0) {
-    int nd = 0, qt = 0;
-    for (int g = 0; g < R; ++g) {
-      nd += X[g] > 0;
-      qt += D[g] > 0;
-    }
+    const int nd = s_nd;
+    int qt = s_nq;
     int qh = 0;
     int ndon = 0;
     int i = 0;
@@ -348,6 +370,8 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     ent_lo[idx] = rlo;
   }
   __syncthreads();
+  // rows: home experts use their own row; the j-th remote expert with tokens
+  // (ascending id) prefetch row E+j while j < B, its home row after that
   for (int idx = tid; idx < R * L2; idx += kSolveThreads) {
     const int d = idx / L2, i = idx - (idx / L2) * L2;
     int row = -1;
@@ -356,6 +380,7 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
         row = d * L + i;
       } else {
         int j = 0;
+#pragma unroll 8
         for (int q = L; q < i; ++q) j += ent_n[d * L2 + q] > 0;
         row = j < B ? E + j : recv_g[d] * L + (i - L);
       }
@@ -368,14 +393,24 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   // lower group's rows first (the rank's home experts or the remote experts
   // that keep home rows), prefetch rows last.  Every active entry gets a
   // visit-order slot (3L per rank); one block-wide scan over all slots gives
-  // each row's start and its index among the rank's active rows.
+  // each row's start and its index among the rank's active rows.  Per rank:
+  // its remote experts and used prefetch rows, counted by one thread.
   const int S3 = 3 * L;
   const int nslot = R * S3;
   for (int i = tid; i < nslot; i += kSolveThreads) {
     ord_len[i] = 0;
     ord_ent[i] = -1;
   }
-  for (int d = tid; d < R; d += kSolveThreads) { nrem[d] = 0; npf[d] = 0; }
+  for (int d = tid; d < R; d += kSolveThreads) {
+    int rem = 0, pfc = 0;
+#pragma unroll 8
+    for (int i = L; i < L2; ++i) {
+      rem += ent_n[d * L2 + i] > 0;
+      pfc += ent_row[d * L2 + i] >= E;
+    }
+    nrem[d] = rem;
+    npf[d] = pfc;
+  }
   __syncthreads();
   for (int idx = tid; idx < R * L2; idx += kSolveThreads) {
     const int n = ent_n[idx];
@@ -390,6 +425,21 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     ord_len[d * S3 + o] = round_up(n, a.tp);
     ord_ent[d * S3 + o] = idx;
   }
+  // prefix of the used prefetch rows over the ranks (one wave)
+  if (tid < 64) {
+    int run = 0;
+    for (int d0 = 0; d0 < R; d0 += 64) {
+      const int d = d0 + tid;
+      const int v = d < R ? npf[d] : 0;
+      int x = v;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (tid >= o) x += y;
+      }
+      if (d < R) pfpre[d] = run + x - v;
+      run += __shfl(x, 63, 64);
+    }
+  }
   __syncthreads();
   int tot_cnt;
   {
@@ -397,9 +447,8 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     const int b0 = min(nslot, tid * per), b1 = min(nslot, b0 + per);
     int sl = 0, sc = 0;
     for (int i = b0; i < b1; ++i) { sl += ord_len[i]; sc += ord_ent[i] >= 0; }
-    int tot_len;
-    int pl = block_exclusive_scan(sl, &tot_len, scan_scratch);
-    int pc = block_exclusive_scan(sc, &tot_cnt, scan_scratch);
+    int pl, pc, tot_len;
+    block_scan2(sl, sc, &pl, &pc, &tot_len, &tot_cnt, scan_scratch);
     for (int i = b0; i < b1; ++i) {          // exclusive prefixes, in place
       const int l = ord_len[i];
       ord_len[i] = pl;
@@ -409,28 +458,29 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     }
   }
   __syncthreads();
-  for (int i = tid; i < nslot; i += kSolveThreads) {
-    const int idx = ord_ent[i];
-    if (idx < 0) continue;
-    const int d = i / S3;
-    const int q = ord_cnt[i] - ord_cnt[d * S3];
-    const int start = ord_len[i] - ord_len[d * S3];
-    const int n = ent_n[idx];
-    const int len = round_up(n, a.tp);
-    const int row = ent_row[idx];
-    const int ie = idx - d * L2;
-    const bool home = ie < L;
-    const int e = home ? d * L + ie : recv_g[d] * L + (ie - L);
-    a.shift[d * E + e] = start - ent_lo[idx];
-    act_row[d * L2 + q] = row;
-    act_end[d * L2 + q] = start + len;
-    act_n[d * L2 + q] = n;
-    if (!home) atomicAdd(&nrem[d], 1);
-    if (row >= E) {
-      a.pf[d * B + (row - E)] = e;
-      atomicAdd(&npf[d], 1);
+  {
+    int pad = 0;
+    for (int i = tid; i < nslot; i += kSolveThreads) {
+      const int idx = ord_ent[i];
+      if (idx < 0) continue;
+      const int d = i / S3;
+      const int q = ord_cnt[i] - ord_cnt[d * S3];
+      const int start = ord_len[i] - ord_len[d * S3];
+      const int n = ent_n[idx];
+      const int len = round_up(n, a.tp);
+      const int row = ent_row[idx];
+      const int ie = idx - d * L2;
+      const bool home = ie < L;
+      const int e = home ? d * L + ie : recv_g[d] * L + (ie - L);
+      a.shift[d * E + e] = start - ent_lo[idx];
+      act_row[d * L2 + q] = row;
+      act_end[d * L2 + q] = start + len;
+      act_n[d * L2 + q] = n;
+      if (row >= E) a.pf[d * B + (row - E)] = e;
+      pad += len - n;
     }
-    if (len > n) atomicAdd(&s_pad, len - n);
+    pad = wave_sum(pad);
+    if ((tid & 63) == 0 && pad) atomicAdd(&s_pad, pad);
   }
   __syncthreads();
   for (int d = tid; d < R; d += kSolveThreads) {
@@ -446,11 +496,13 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   for (int i = tid; i < R * B; i += kSolveThreads) {
     const int d = i / B, j = i - (i / B) * B;
     if (j >= npf[d]) a.pf[i] = -1;
+    else a.aux[a.ax.pf + pfpre[d] + j] = i;      // used prefetch slots in (d, j) order
   }
   for (int i = tid; i < R * L2; i += kSolveThreads) {
     const int d = i / L2, q = i - (i / L2) * L2;
     a.aux[a.ax.act + i] = q < nact[d] ? act_row[i] : -1;
   }
+  if (tid == 0) a.aux[a.ax.pf_n] = R > 0 ? pfpre[R - 1] + npf[R - 1] : 0;
 
   // Phase G: cu_seqlens and seg_tokens for every (rank, row).
   const int EB = E + B;
@@ -474,14 +526,6 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     a.segn[idx] = n;
   }
 
-  // Phase G2: used prefetch slots in (d, j) order.
-  if (tid == 0) {
-    int k = 0;
-    for (int d = 0; d < R; ++d)
-      for (int j = 0; j < npf[d]; ++j) a.aux[a.ax.pf + k++] = d * B + j;
-    a.aux[a.ax.pf_n] = k;
-  }
-
   // Phase G3: holders of every home expert that has prefetch copies, in
   // ascending rank (the reduce_grad order).
   for (int e = tid; e < E; e += kSolveThreads) {
@@ -496,9 +540,8 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     const int e = tid;
     const int has = (e < E && hcount[e] > 0) ? 1 : 0;
     const int cnt = e < E ? hcount[e] : 0;
-    int nexp, nhold;
-    const int q = block_exclusive_scan(has, &nexp, scan_scratch);
-    const int first = block_exclusive_scan(cnt, &nhold, scan_scratch);
+    int q, first, nexp, nhold;
+    block_scan2(has, cnt, &q, &first, &nexp, &nhold, scan_scratch);
     if (has) {
       const int g = e / L, i = e - g * L;
       a.aux[a.ax.dup_e + q] = e;
@@ -559,19 +602,41 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
   const bool tab = a.R * a.E <= kShiftLds && npc <= kPiecesLds;
   if (!err) {
     for (int i = tid; i < 4 * a.E; i += kPlanChunk) mask[i / a.E][i % a.E] = 0ull;
+    // this token's expert ids, loaded once
+    int ids[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) ids[k] = (s < a.S && k < a.K) ? a.topk[tok * a.K + k] : 0;
     // line position of this chunk's first token of expert e: the expert's
     // line start + tokens of lower ranks + tokens of earlier chunks of rank r
     const int32_t* gbase = a.cc + ((int64_t)r * a.nch + ch) * a.E;
-    for (int i = tid; i < a.E; i += kPlanChunk)
-      s_base[i] = gbase[i] + a.line[i] + a.rankpre[r * a.E + i];
+    for (int i = tid; i < a.E; i += kPlanChunk) {
+      int v = gbase[i] + a.line[i];
+#pragma unroll 8
+      for (int q = 0; q < r; ++q) v += a.counts[q * a.E + i];
+      s_base[i] = v;
+    }
     for (int i = tid; i < a.R; i += kPlanChunk) s_np[i] = a.npieces[i];
     if (tab) {
-      for (int i = tid; i < a.R * a.E; i += kPlanChunk) s_shift[i] = a.shift[i];
+      for (int i0 = tid; i0 < a.R * a.E; i0 += 4 * kPlanChunk) {
+        int v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * kPlanChunk;
+          v[u] = i < a.R * a.E ? a.shift[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * kPlanChunk;
+          if (i < a.R * a.E) s_shift[i] = v[u];
+        }
+      }
       for (int i = tid; i < npc; i += kPlanChunk) s_pieces[i] = a.pieces[i];
     }
     __syncthreads();
     if (s < a.S)
-      for (int k = 0; k < a.K; ++k) atomicOr(&mask[w][a.topk[tok * a.K + k]], bit);
+#pragma unroll
+      for (int k = 0; k < kMaxK; ++k)
+        if (k < a.K) atomicOr(&mask[w][ids[k]], bit);
     __syncthreads();
     if (s < a.S) {
       for (int k = 0; k < a.K; ++k) {
@@ -639,7 +704,7 @@ hipError_t launch_plan(const Ctx& c, const int32_t* topk, const int32_t* tpe,
   a.R = d.R; a.S = d.S; a.K = d.K; a.E = d.E; a.B = d.B; a.L = d.L; a.tp = d.tp;
   a.nch = d.nch; a.NvS = (int)d.NvS; a.max_tiles = d.max_tiles;
   a.topk = topk; a.tpe = tpe;
-  a.cc = c.cc; a.chunk_err = c.chunk_err; a.rankpre = c.rankpre; a.shift = c.shift;
+  a.cc = c.cc; a.chunk_err = c.chunk_err; a.shift = c.shift;
   a.pieces = c.pieces; a.npieces = c.npieces; a.line = c.line;
   a.counts = p.counts; a.dest = p.dest; a.src = p.src; a.cu = p.cu_seqlens;
   a.segn = p.seg_tokens; a.pf = p.prefetch_src; a.stats = p.stats; a.aux = p.aux;
