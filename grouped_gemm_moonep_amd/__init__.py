@@ -115,6 +115,20 @@ class Buffer:
                    "moonep_plan")
         return plan
 
+    def plan_noalloc(self, topk, tokens_per_expert=None, plan=None):
+        """moonep_plan_noalloc: the same plan as `plan`, computed without the
+        handle's scratch and without allocating device memory (the library's
+        fixed per-GPU scratch array; concurrent calls on one GPU race).  Only
+        `plan=None` allocates here, in Python, for the plan arrays."""
+        plan = plan or self.new_plan()
+        R, S, K, E = self.R, self.S, self.K, self.E
+        p_topk = _dev_ptr(topk, torch.int32, (R, S, K), "topk")
+        p_tpe = _dev_ptr(tokens_per_expert, torch.int32, (R, E), "tokens_per_expert", True)
+        _abi.check(lib().moonep_plan_noalloc(ctypes.byref(self.cfg), p_topk, p_tpe,
+                                             ctypes.byref(plan.struct), _stream()),
+                   "moonep_plan_noalloc")
+        return plan
+
     def copy_rows(self, plan, src_nvs, dst_nvs=None):
         """The used slots of every rank from src_nvs to dst_nvs (moonep_copy_rows)."""
         R, NvS = self.R, self.NvS

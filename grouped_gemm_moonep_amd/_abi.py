@@ -13,7 +13,8 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoonep.so")
 
-MOONEP_OK, MOONEP_ERR_ARG, MOONEP_ERR_CONFIG, MOONEP_ERR_MODE, MOONEP_ERR_HIP, MOONEP_ERR_NOMEM = range(6)
+(MOONEP_OK, MOONEP_ERR_ARG, MOONEP_ERR_CONFIG, MOONEP_ERR_MODE, MOONEP_ERR_HIP, MOONEP_ERR_NOMEM,
+ MOONEP_ERR_SCRATCH) = range(7)
 STAT_ERROR, STAT_DUPS, STAT_MAX_LOAD, STAT_DONATIONS, STAT_PAD_ROWS, STAT_MAXVIO = range(6)
 STAT_FIXED = 8
 PLAN_ARRAYS = ["counts", "dest", "src", "cu_seqlens", "seg_tokens", "prefetch_src", "stats", "aux"]
@@ -66,6 +67,8 @@ def lib():
         "moonep_create": (i32, [ctypes.POINTER(MoonepConfig), ctypes.POINTER(vp)]),
         "moonep_destroy": (i32, [vp]),
         "moonep_plan": (i32, [vp, vp, vp, ctypes.POINTER(MoonepPlan), vp]),
+        "moonep_plan_noalloc": (i32, [ctypes.POINTER(MoonepConfig), vp, vp,
+                                      ctypes.POINTER(MoonepPlan), vp]),
         "moonep_dispatch": (i32, [vp, ctypes.POINTER(MoonepPlan), vp, i32, vp, vp, vp, vp]),
         "moonep_combine": (i32, [vp, ctypes.POINTER(MoonepPlan), vp, i32, vp, vp, vp, vp]),
         "moonep_copy_rows": (i32, [vp, ctypes.POINTER(MoonepPlan), vp, i32, vp, vp]),

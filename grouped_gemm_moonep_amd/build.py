@@ -18,7 +18,8 @@ REPO = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoonep.so")
-SOURCES = ["api.hip", "plan.hip", "move.hip", "gemm.hip", "gemm_bwd.hip", "symbuf.hip"]
+SOURCES = ["api.hip", "plan.hip", "plan_noalloc.hip", "move.hip", "gemm.hip", "gemm_bwd.hip",
+           "symbuf.hip"]
 ARCH = "gfx950"
 
 

@@ -144,6 +144,8 @@ const char* moonep_status_string(moonep_status_t s) {
     case MOONEP_ERR_MODE: return "training call needs B == E/R";
     case MOONEP_ERR_HIP: return "HIP runtime error";
     case MOONEP_ERR_NOMEM: return "device allocation failed";
+    case MOONEP_ERR_SCRATCH:
+      return "configuration needs more planning scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }

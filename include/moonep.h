@@ -48,7 +48,9 @@ enum {
   MOONEP_ERR_CONFIG = 2,  /* configuration outside the supported range     */
   MOONEP_ERR_MODE = 3,    /* training call with B != E/R                   */
   MOONEP_ERR_HIP = 4,     /* a HIP runtime call or kernel launch failed    */
-  MOONEP_ERR_NOMEM = 5    /* scratch allocation in moonep_create failed    */
+  MOONEP_ERR_NOMEM = 5,   /* scratch allocation in moonep_create failed    */
+  MOONEP_ERR_SCRATCH = 6  /* moonep_plan_noalloc: the configuration needs
+                             more planning scratch than the library holds  */
 };
 
 /* Problem sizes, in the README's notation ("Usage > Integration"):
@@ -138,6 +140,25 @@ moonep_status_t moonep_destroy(moonep_handle_t h);
 moonep_status_t moonep_plan(moonep_handle_t h, const int32_t* topk,
                             const int32_t* tokens_per_expert,
                             const moonep_plan_t* plan, hipStream_t stream);
+
+/* Planning without a handle and without any allocation, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, kernels and
+ * results as moonep_plan (every plan array bit-identical), with the
+ * configuration passed directly; the planning scratch is a fixed array of
+ * MOONEP_NOALLOC_SCRATCH_BYTES in the library's device memory, one per GPU,
+ * which the GPU holds until the process ends.  The scratch needed, in int32
+ * elements each rounded up to 64, is R*ceil(S/256)*E + R*E + 2*R*(R+1)
+ * + R + E + R*ceil(S/256); MOONEP_ERR_SCRATCH (nothing enqueued) when it
+ * exceeds the array (e.g. R=8, E=256 fits up to S of about 64000).  Calls
+ * that overlap on one GPU (different streams or host threads) share the
+ * array and race; calls on one stream are ordered.  The first call with a
+ * device current looks the array's device address up (hipGetSymbolAddress);
+ * no call allocates or frees memory. */
+#define MOONEP_NOALLOC_SCRATCH_BYTES (2 * 1024 * 1024)
+moonep_status_t moonep_plan_noalloc(const moonep_config_t* cfg, const int32_t* topk,
+                                    const int32_t* tokens_per_expert,
+                                    const moonep_plan_t* plan, hipStream_t stream);
 
 /* Dispatch (README "API guide > dispatch fwd"; also "combine bwd", which is a
  * re-dispatch of the output gradient with the saved plan).

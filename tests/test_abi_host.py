@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
 def test_version_and_status_strings():
     lib = _abi.lib()
     assert lib.moonep_abi_version() == 1
-    for s in range(6):
+    for s in range(7):
         assert _abi.status_string(s)
     assert _abi.status_string(99) == "unknown status"
 
@@ -111,6 +111,32 @@ def test_null_arguments_rejected_on_host():
                                        None) == ERR
     assert lib.moonep_expert_ffn_bwd_views(None, ctypes.byref(plan), -1, None, None, P3(), None,
                                            None, None, None, None) == ERR
+
+
+def test_noalloc_plan_checks_on_host():
+    """moonep_plan_noalloc rejects, before touching a GPU: a bad configuration,
+    missing or misaligned pointers, and a configuration whose planning
+    scratch exceeds the library's fixed array (MOONEP_ERR_SCRATCH)."""
+    lib = _abi.lib()
+    w = synth.WORKLOADS["fwd_r8_s4096_k8_e256"]
+    fake = ctypes.c_void_p(0x10000)          # never dereferenced on these paths
+    full = _abi.MoonepPlan(*([0x10000] * len(_abi.PLAN_ARRAYS)))
+    assert lib.moonep_plan_noalloc(ctypes.byref(_cfg(w, K=0)), fake, None, ctypes.byref(full),
+                                   None) == _abi.MOONEP_ERR_CONFIG
+    assert lib.moonep_plan_noalloc(None, fake, None, ctypes.byref(full),
+                                   None) == _abi.MOONEP_ERR_CONFIG
+    assert lib.moonep_plan_noalloc(ctypes.byref(_cfg(w)), None, None, ctypes.byref(full),
+                                   None) == _abi.MOONEP_ERR_ARG
+    assert lib.moonep_plan_noalloc(ctypes.byref(_cfg(w)), ctypes.c_void_p(0x10002), None,
+                                   ctypes.byref(full), None) == _abi.MOONEP_ERR_ARG
+    assert lib.moonep_plan_noalloc(ctypes.byref(_cfg(w)), fake, None,
+                                   ctypes.byref(_abi.MoonepPlan()), None) == _abi.MOONEP_ERR_ARG
+    # R * ceil(S/256) * E int32 of chunk counts alone: 8 * 782 * 256 > 2 MiB / 4
+    big = _cfg(w, S=200_000, H=64, Hp=64)
+    assert lib.moonep_nvs(ctypes.byref(big)) > 0
+    assert lib.moonep_plan_noalloc(ctypes.byref(big), fake, None, ctypes.byref(full),
+                                   None) == _abi.MOONEP_ERR_SCRATCH
+    assert "scratch" in _abi.status_string(_abi.MOONEP_ERR_SCRATCH)
 
 
 def test_dlpack_wrapper_layout():
