@@ -192,6 +192,7 @@ moonep_status_t moonep_create(const moonep_config_t* cfg, moonep_handle_t* out) 
       {&c.npieces, d.R},
       {&c.line, d.E},
       {&c.chunk_err, (int64_t)d.R * d.nch},
+      {&c.efix, 2LL * d.E},
   };
   for (auto& a : allocs) {
     if (hipMalloc((void**)a.p, (size_t)a.n * sizeof(int32_t)) != hipSuccess) {
@@ -207,7 +208,7 @@ moonep_status_t moonep_destroy(moonep_handle_t h) {
   if (!h) return MOONEP_OK;
   Ctx& c = h->c;
   int32_t* ptrs[] = {c.cc, c.shift, c.pieces, c.npieces, c.line,
-                     c.chunk_err};
+                     c.chunk_err, c.efix};
   hipError_t err = hipSuccess;
   for (int32_t* p : ptrs)
     if (p) {

@@ -52,6 +52,8 @@ struct Ctx {
   int32_t* npieces;   // [R]
   int32_t* line;      // [E] line start a_e
   int32_t* chunk_err; // [R][nch] routing error bits found per chunk
+  int32_t* efix;      // [E][2] (rank, slot - line position) of an expert whose tokens all
+                      // go to one rank, rank -1 for an expert split over ranks
 };
 
 bool dims_from_config(const moonep_config_t* cfg, Dims* out);

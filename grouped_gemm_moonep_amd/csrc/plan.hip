@@ -49,6 +49,7 @@ struct PlanArgs {
   int32_t* pieces;
   int32_t* npieces;
   int32_t* line;
+  int32_t* efix;
   int32_t* counts;
   int32_t* dest;
   int32_t* src;
@@ -174,7 +175,6 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     s_err = 0; s_maxload = 0; s_ndon = 0; s_dups = 0; s_pad = 0; s_nd = 0; s_nq = 0;
   }
   for (int e = tid; e < E; e += kSolveThreads) T[e] = 0;
-  for (int g = tid; g < R; g += kSolveThreads) W[g] = 0;
   __syncthreads();
 
   // Phase A: counts per (r, e), the exclusive per-chunk prefix (in place) and
@@ -245,19 +245,39 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
 
   // Phase C: line start of every expert (experts of a group by (T, id)), the
   // group loads W_g and the largest load.
-  for (int e = tid; e < E; e += kSolveThreads) {
-    const int g = e / L;
-    const int te = T[e];
-    int acc = 0;
-#pragma unroll 8
-    for (int f = g * L; f < (g + 1) * L; ++f) {
-      const int tf = T[f];
-      acc += (tf < te || (tf == te && f < e)) ? tf : 0;
+  // Four lanes per expert (adjacent lanes of one wave), each scanning a
+  // quarter of the group, then summed with shuffles; the group loads from
+  // the same quarters (lanes of the group's first expert).
+  {
+    int mx = 0;
+    for (int e0 = 0; e0 < E; e0 += kSolveThreads / 4) {
+      const int e = e0 + (tid >> 2), part = tid & 3;
+      int acc = 0, tot = 0, te = 0;
+      if (e < E) {
+        const int g = e / L;
+        te = T[e];
+        const int f0 = g * L + (part * L) / 4, f1 = g * L + ((part + 1) * L) / 4;
+#pragma unroll 4
+        for (int f = f0; f < f1; ++f) {
+          const int tf = T[f];
+          acc += (tf < te || (tf == te && f < e)) ? tf : 0;
+          tot += tf;
+        }
+      }
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      tot += __shfl_xor(tot, 1, 64);
+      tot += __shfl_xor(tot, 2, 64);
+      if (e < E && part == 0) {
+        aline[e] = acc;
+        a.line[e] = acc;
+        if (e % L == 0) W[e / L] = tot;
+      }
+      mx = max(mx, te);
     }
-    aline[e] = acc;
-    a.line[e] = acc;
-    atomicAdd(&W[g], te);
-    atomicMax(&s_maxload, te);
+    // the largest load: a wave maximum, then one LDS atomic per wave
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
+    if ((tid & 63) == 0 && mx > 0) atomicMax(&s_maxload, mx);
   }
   __syncthreads();
 
@@ -402,14 +422,8 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     ord_ent[i] = -1;
   }
   for (int d = tid; d < R; d += kSolveThreads) {
-    int rem = 0, pfc = 0;
-#pragma unroll 8
-    for (int i = L; i < L2; ++i) {
-      rem += ent_n[d * L2 + i] > 0;
-      pfc += ent_row[d * L2 + i] >= E;
-    }
-    nrem[d] = rem;
-    npf[d] = pfc;
+    nrem[d] = 0;
+    npf[d] = 0;
   }
   __syncthreads();
   for (int idx = tid; idx < R * L2; idx += kSolveThreads) {
@@ -418,13 +432,17 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     const int d = idx / L2, i = idx - (idx / L2) * L2;
     const int g = recv_g[d];
     const bool home_first = g < 0 || d < g;
+    const bool pf = ent_row[idx] >= E;
     int o;
     if (i < L) o = (home_first ? 0 : L) + i;
-    else if (ent_row[idx] >= E) o = 2 * L + (i - L);
+    else if (pf) o = 2 * L + (i - L);
     else o = (home_first ? L : 0) + (i - L);
     ord_len[d * S3 + o] = round_up(n, a.tp);
     ord_ent[d * S3 + o] = idx;
+    if (i >= L) atomicAdd(&nrem[d], 1);      // the rank's remote experts
+    if (pf) atomicAdd(&npf[d], 1);           // of which in prefetch rows
   }
+  __syncthreads();
   // prefix of the used prefetch rows over the ranks (one wave)
   if (tid < 64) {
     int run = 0;
@@ -473,6 +491,9 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
       const bool home = ie < L;
       const int e = home ? d * L + ie : recv_g[d] * L + (ie - L);
       a.shift[d * E + e] = start - ent_lo[idx];
+      // an expert all of whose tokens land here: the assignment needs no piece search
+      a.efix[2 * e] = n == T[e] ? d : -1;
+      if (n == T[e]) a.efix[2 * e + 1] = start - ent_lo[idx];
       act_row[d * L2 + q] = row;
       act_end[d * L2 + q] = start + len;
       act_n[d * L2 + q] = n;
@@ -531,8 +552,8 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   for (int e = tid; e < E; e += kSolveThreads) {
     const int g = e / L, i = e - g * L;
     int cnt = 0;
-    for (int d = 0; d < R; ++d)
-      if (recv_g[d] == g && ent_row[d * L2 + L + i] >= E) ++cnt;
+#pragma unroll 8
+    for (int d = 0; d < R; ++d) cnt += (recv_g[d] == g && ent_row[d * L2 + L + i] >= E) ? 1 : 0;
     hcount[e] = cnt;
   }
   __syncthreads();
@@ -548,6 +569,7 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
       a.aux[a.ax.dup_first + q] = first;
       a.aux[a.ax.dup_cnt + q] = cnt;
       int k = 0;
+#pragma unroll 8
       for (int d = 0; d < R; ++d) {
         const int row = ent_row[d * L2 + L + i];
         if (recv_g[d] == g && row >= E) a.aux[a.ax.hold + first + k++] = d * B + (row - E);
@@ -580,10 +602,10 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
     // the grid's extra column: rank blockIdx.y's grouped-GEMM tile schedule,
     // built from plan_solve's segments alongside the token assignment
     __shared__ int wsum[4];
+    __shared__ TileSchedLds sl;
     build_tile_schedule(a.aux + a.ax.act, a.cu, a.segn, a.aux + a.ax.tiles,
                         a.aux + a.ax.ntiles, a.aux + a.ax.nfull, blockIdx.y, 2 * a.L,
-                        a.E + a.B, a.tp, a.max_tiles,
-                        wsum);
+                        a.E + a.B, a.tp, a.max_tiles, wsum, sl);
     return;
   }
   __shared__ unsigned long long mask[4][kMaxE];
@@ -591,6 +613,8 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
   __shared__ int s_shift[kShiftLds];
   __shared__ int s_pieces[kPiecesLds];
   __shared__ int s_np[kMaxR];
+  __shared__ int s_plo[kPlanChunk], s_phi[kPlanChunk];
+  __shared__ int s_efix[2 * kMaxE];
   const int ch = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
   const int err = a.stats[MOONEP_STAT_ERROR];
   const int s = ch * kPlanChunk + tid;
@@ -606,6 +630,13 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
     int ids[kMaxK];
 #pragma unroll
     for (int k = 0; k < kMaxK; ++k) ids[k] = (s < a.S && k < a.K) ? a.topk[tok * a.K + k] : 0;
+    // the active row whose padding this thread clears (rows ch, ch + nch, ... of the rank:
+    // thread t takes row ch + t nch) and the end of the rank's last segment, loaded up front
+    // so that their latency overlaps the staging below
+    const int L2 = 2 * a.L, EB = a.E + a.B;
+    const int q_pad = ch + tid * a.nch;
+    const int pad_row = q_pad < L2 ? a.aux[a.ax.act + r * L2 + q_pad] : -1;
+    const int last = a.cu[r * EB + EB - 1];
     // line position of this chunk's first token of expert e: the expert's
     // line start + tokens of lower ranks + tokens of earlier chunks of rank r
     const int32_t* gbase = a.cc + ((int64_t)r * a.nch + ch) * a.E;
@@ -616,6 +647,7 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
       s_base[i] = v;
     }
     for (int i = tid; i < a.R; i += kPlanChunk) s_np[i] = a.npieces[i];
+    for (int i = tid; i < 2 * a.E; i += kPlanChunk) s_efix[i] = a.efix[i];
     if (tab) {
       for (int i0 = tid; i0 < a.R * a.E; i0 += 4 * kPlanChunk) {
         int v[4];
@@ -637,47 +669,93 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
 #pragma unroll
       for (int k = 0; k < kMaxK; ++k)
         if (k < a.K) atomicOr(&mask[w][ids[k]], bit);
+    // the padding range of this thread's row (in flight during the assignment)
+    if (pad_row >= 0) {
+      const int end = a.cu[r * EB + pad_row];
+      const int n = a.segn[r * EB + pad_row];
+      s_plo[tid] = end - round_up(n, a.tp) + n;
+      s_phi[tid] = end;
+    } else {
+      s_plo[tid] = 0;
+      s_phi[tid] = 0;
+    }
     __syncthreads();
     if (s < a.S) {
-      for (int k = 0; k < a.K; ++k) {
-        const int e = a.topk[tok * a.K + k];
+      // unrolled over k with the ids in registers, so the LDS lookups of a
+      // token's K slots overlap instead of running one chain after another;
+      // the token's K destinations leave as 16-byte stores when K % 4 == 0
+      // (and dest is 16-byte aligned)
+      int dk[kMaxK];
+#pragma unroll
+      for (int k = 0; k < kMaxK; ++k) {
+        if (k >= a.K) break;
+        const int e = ids[k];
         int below = __popcll(mask[w][e] & (bit - 1));
         for (int v = 0; v < w; ++v) below += __popcll(mask[v][e]);
         const int pos = s_base[e] + below;
-        const int g = e / a.L;
-        const int32_t* pg = (tab ? (const int32_t*)s_pieces : a.pieces) + (int64_t)g * (a.R + 1) * 2;
-        const int np = s_np[g];
-        int d = pg[1];
-        for (int p = 0; p < np; ++p) {
-          if (pos < pg[2 * p]) { d = pg[2 * p + 1]; break; }
+        int d = s_efix[2 * e];
+        int slot;
+        if (d >= 0) {
+          slot = s_efix[2 * e + 1] + pos;          // the expert's tokens all go to rank d
+        } else {
+          // the expert is split over ranks: the piece of its group's line holding pos
+          const int g = e / a.L;
+          const int32_t* pg = (tab ? (const int32_t*)s_pieces : a.pieces) + (int64_t)g * (a.R + 1) * 2;
+          const int np = s_np[g];
+          // the first piece whose end lies past pos: count the pieces ending at or
+          // before it (ends ascend), eight independent reads at a time
+          int cnt = 0;
+          for (int p0 = 0; p0 < np; p0 += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int p = p0 + u;
+              const int hi = p < np ? pg[2 * p] : 0x7FFFFFFF;
+              cnt += pos >= hi ? 1 : 0;
+            }
+          }
+          d = cnt < np ? pg[2 * cnt + 1] : pg[1];
+          slot = (unsigned)d < (unsigned)a.R
+                     ? (tab ? s_shift[d * a.E + e] : a.shift[d * a.E + e]) + pos : -1;
         }
         const int32_t id = (int32_t)(tok * a.K + k);
-        if ((unsigned)d >= (unsigned)a.R) {       // cannot happen for a valid plan
-          a.dest[id] = r * a.NvS + s * a.K + k;
-          continue;
+        if ((unsigned)slot < (unsigned)a.NvS) {
+          dk[k] = d * a.NvS + slot;
+          a.src[(int64_t)d * a.NvS + slot] = id;
+        } else {
+          dk[k] = r * a.NvS + s * a.K + k;          // cannot happen for a valid plan
         }
-        const int slot = (tab ? s_shift[d * a.E + e] : a.shift[d * a.E + e]) + pos;
-        if ((unsigned)slot >= (unsigned)a.NvS) {  // cannot happen for a valid plan
-          a.dest[id] = r * a.NvS + s * a.K + k;
-          continue;
-        }
-        a.dest[id] = d * a.NvS + slot;
-        a.src[(int64_t)d * a.NvS + slot] = id;
+      }
+      int32_t* drow = a.dest + tok * a.K;
+      if ((a.K & 3) == 0 && ((uintptr_t)a.dest & 15) == 0) {
+        typedef int i32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int k = 0; k < kMaxK; k += 4)
+          if (k < a.K) *(i32x4*)(drow + k) = i32x4{dk[k], dk[k + 1], dk[k + 2], dk[k + 3]};
+      } else {
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k)
+          if (k < a.K) drow[k] = dk[k];
       }
     }
-    // padding slots of this rank's active rows handled by this chunk
-    const int L2 = 2 * a.L, EB = a.E + a.B;
-    for (int q = ch; q < L2; q += a.nch) {
-      const int row = a.aux[a.ax.act + r * L2 + q];
-      if (row < 0) break;
-      const int end = a.cu[r * EB + row];
-      const int n = a.segn[r * EB + row];
-      const int len = round_up(n, a.tp);
-      for (int i = end - len + n + tid; i < end; i += kPlanChunk)
-        a.src[(int64_t)r * a.NvS + i] = -1;
+    // padding slots of this rank's active rows handled by this chunk (rows ch, ch + nch,
+    // ...; thread t found the range of row ch + t nch): the whole workgroup clears one
+    // row's range after the other
+    const int npad = L2 > ch ? min((L2 - ch + a.nch - 1) / a.nch, kPlanChunk) : 0;
+    for (int t = 0; t < npad; ++t) {
+      const int lo = s_plo[t], hi = s_phi[t];
+      for (int i = lo + tid; i < hi; i += kPlanChunk) a.src[(int64_t)r * a.NvS + i] = -1;
+    }
+    // rows past the first 256 of the chunk (more than 256 nch active rows), a thread each
+    for (int q0 = kPlanChunk; ch + q0 * a.nch < L2; q0 += kPlanChunk) {
+      const int q = ch + (q0 + tid) * a.nch;
+      const int row = q < L2 ? a.aux[a.ax.act + r * L2 + q] : -1;
+      if (row >= 0) {
+        const int end = a.cu[r * EB + row];
+        const int n = a.segn[r * EB + row];
+        for (int i = end - round_up(n, a.tp) + n; i < end; ++i) a.src[(int64_t)r * a.NvS + i] = -1;
+      }
     }
     // this chunk's share of the tail past the last segment
-    const int last = a.cu[r * EB + EB - 1];
     const int span = (a.NvS - last + a.nch - 1) / a.nch;
     const int t0 = last + ch * span;
     const int t1 = min(a.NvS, t0 + span);
@@ -705,7 +783,7 @@ hipError_t launch_plan(const Ctx& c, const int32_t* topk, const int32_t* tpe,
   a.nch = d.nch; a.NvS = (int)d.NvS; a.max_tiles = d.max_tiles;
   a.topk = topk; a.tpe = tpe;
   a.cc = c.cc; a.chunk_err = c.chunk_err; a.shift = c.shift;
-  a.pieces = c.pieces; a.npieces = c.npieces; a.line = c.line;
+  a.pieces = c.pieces; a.npieces = c.npieces; a.line = c.line; a.efix = c.efix;
   a.counts = p.counts; a.dest = p.dest; a.src = p.src; a.cu = p.cu_seqlens;
   a.segn = p.seg_tokens; a.pf = p.prefetch_src; a.stats = p.stats; a.aux = p.aux;
   a.ax = d.aux;

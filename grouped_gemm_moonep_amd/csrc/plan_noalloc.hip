@@ -1,6 +1,6 @@
 // moonep_plan without a handle and without allocating: the planning scratch
 // (per-chunk expert counts, slot shifts, line pieces, line starts, per-chunk
-// error bits) lives in one file-scope device array instead
+// error bits, per-expert destinations) lives in one file-scope device array instead
 // of the handle's device allocations, for callers that cannot allocate device
 // memory (code under HIP graph capture, tight serving loops, harnesses that
 // forbid allocation).  The kernels are the planner's own (launch_plan); only
@@ -33,7 +33,7 @@ int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }   // 256-byte pieces
 // int32 elements of every planning scratch array of `d`, in the order they
 // are carved out of the array.
 struct Carve {
-  int64_t n[6];
+  int64_t n[7];
   int64_t total() const {
     int64_t t = 0;
     for (int64_t v : n) t += pad64(v);
@@ -43,7 +43,7 @@ struct Carve {
 
 Carve carve(const Dims& d) {
   return Carve{{(int64_t)d.R * d.nch * d.E, (int64_t)d.R * d.E, (int64_t)d.R * (d.R + 1) * 2,
-                (int64_t)d.R, (int64_t)d.E, (int64_t)d.R * d.nch}};
+                (int64_t)d.R, (int64_t)d.E, (int64_t)d.R * d.nch, 2LL * d.E}};
 }
 
 bool plan_arrays_ok(const moonep_plan_t* p) {
@@ -93,9 +93,10 @@ extern "C" moonep_status_t moonep_plan_noalloc(const moonep_config_t* cfg, const
   c.d = d;
   c.device = 0;
   c.num_cu_device = 0;
-  int32_t** dst[6] = {&c.cc, &c.shift, &c.pieces, &c.npieces, &c.line, &c.chunk_err};
+  int32_t** dst[7] = {&c.cc, &c.shift, &c.pieces, &c.npieces, &c.line, &c.chunk_err,
+                       &c.efix};
   int64_t off = 0;
-  for (int i = 0; i < 6; ++i) {
+  for (int i = 0; i < 7; ++i) {
     *dst[i] = base + off;
     off += pad64(cv.n[i]);
   }

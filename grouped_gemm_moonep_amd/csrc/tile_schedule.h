@@ -48,11 +48,18 @@ __device__ __forceinline__ int block_scan256(int v, int* total, int (&wsum)[4]) 
   return before + x - v;
 }
 
+// Per pass of 256 active rows: each row's first full tile, end of its full tiles, row,
+// segment end, padded length and group size, so that all threads can write the tiles.
+struct TileSchedLds {
+  int t0[256], tend[256], row[256], end[256], len[256], grp[256];
+};
+
 __device__ __forceinline__ void build_tile_schedule(const int32_t* act, const int32_t* cu,
                                                     const int32_t* segn, int32_t* tiles,
                                                     int32_t* ntiles, int32_t* nfull, int d,
                                                     int L2, int EB,
-                                                    int tp, int max_tiles, int (&wsum)[4]) {
+                                                    int tp, int max_tiles, int (&wsum)[4],
+                                                    TileSchedLds& sl) {
   const int tid = threadIdx.x;
   int32_t* rank_tiles = tiles + (int64_t)d * max_tiles * 4;
   auto put = [&](int t, int row, int m0, int m1, int gs, int gm) {
@@ -79,12 +86,29 @@ __device__ __forceinline__ void build_tile_schedule(const int32_t* act, const in
     const int t0 = nfull_all + block_scan256(nf, &total, wsum);
     const int ng = (nf + kGroupMax - 1) / kGroupMax;
     const int g = ng > 0 ? (nf + ng - 1) / ng : 1;      // group size
-    for (int j = 0; j < nf; ++j) {
-      const int m = end - len + j * kTileM;
-      const int gs = t0 + j / g * g;
-      put(t0 + j, row, m, m + kTileM < end ? m + kTileM : end, gs, min(g, t0 + nf - gs));
+    sl.t0[tid] = t0;
+    sl.tend[tid] = t0 + nf;
+    sl.row[tid] = row;
+    sl.end[tid] = end;
+    sl.len[tid] = len;
+    sl.grp[tid] = g;
+    __syncthreads();
+    // every thread writes tiles t, t + 256, ...: the row of tile t is the first
+    // one whose tiles end past t (one segment can hold hundreds of tiles)
+    for (int t = nfull_all + tid; t < nfull_all + total; t += 256) {
+      int lo = 0, hi = 255;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sl.tend[mid] > t) hi = mid;
+        else lo = mid + 1;
+      }
+      const int j = t - sl.t0[lo], gq = sl.grp[lo], eq = sl.end[lo];
+      const int m = eq - sl.len[lo] + j * kTileM;
+      const int gs = sl.t0[lo] + j / gq * gq;
+      put(t, sl.row[lo], m, m + kTileM < eq ? m + kTileM : eq, gs, min(gq, sl.tend[lo] - gs));
     }
     nfull_all += total;
+    __syncthreads();                               // sl is rewritten by the next pass
   }
   // part 2: short tiles, in pairs
   int nshort_all = 0;
