@@ -28,7 +28,6 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, const Ring& smem, 
   lb.init(weight_row(a, 0, d, tl.row) + n0, weight_row(a, 1, d, tl.row) + n0, a.Hp, a.H, nvh,
           nvh);
   f32x16 acc[MI][4];
-  zero_acc<MI>(acc);
   gemm_loop<MI>(la, lb, smem, a.H / BK, acc, wm * 32 * MI, nrow);
 
   // SwiGLU epilogue: blocks j = 0,1 are gate, j = 2,3 the matching up; the
@@ -76,7 +75,6 @@ __device__ __forceinline__ void down_tile(const FfnArgs& a, const Ring& smem, in
   la.init(a.zin + ((int64_t)d * a.NvS + tl.m0) * a.Hp, a.Hp, rows_valid);
   lb.init(weight_row(a, 2, d, tl.row) + (int64_t)n0 * a.Hp, a.Hp, cols_valid);
   f32x16 acc[MI][4];
-  zero_acc<MI>(acc);
   gemm_loop<MI>(la, lb, smem, a.Hp / BK, acc, wm * 32 * MI, nrow);
 
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;

@@ -33,7 +33,6 @@ __device__ __forceinline__ void bwd_dz_tile(const FfnArgs& a, const Ring& smem, 
   const uint16_t* wd = weight_row(a, 2, d, tl.row) + n0;
   lb.init(wd, wd + 128, a.Hp, a.H, nv0, nv1);
   f32x16 acc[MI][4];
-  zero_acc<MI>(acc);
   gemm_loop<MI>(la, lb, smem, a.H / BK, acc, wm * 32 * MI, nrow);
 
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
@@ -70,7 +69,6 @@ __device__ __forceinline__ void bwd_gu_tile(const FfnArgs& a, const Ring& smem, 
   lb.init(weight_row(a, 0, d, tl.row) + n0, weight_row(a, 1, d, tl.row) + n0, a.Hp, a.H, nvh,
           nvh);
   f32x16 acc[MI][4];
-  zero_acc<MI>(acc);
   gemm_loop<MI>(la, lb, smem, a.H / BK, acc, wm * 32 * MI, nrow);
 
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
@@ -138,7 +136,6 @@ __device__ __forceinline__ void bwd_dx_tile(const FfnArgs& a, const Ring& smem, 
   lb.init(weight_row(a, 0, d, tl.row) + (int64_t)n0 * a.Hp,
           weight_row(a, 1, d, tl.row) + (int64_t)n0 * a.Hp, a.Hp, cols_valid, a.Hp);
   f32x16 acc[MI][4];
-  zero_acc<MI>(acc);
   gemm_loop<MI>(la, lb, smem, 2 * a.Hp / BK, acc, wm * 32 * MI, nrow);
 
   const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
@@ -226,7 +223,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   la.init(A, A + 128, a.H, ntok, mv0, mv1);
   lb.init(Bm, Bm + 128, a.Hp, ntok, nv0, nv1);
   f32x16 acc[4][4];
-  zero_acc<4>(acc);
   gemm_loop<4>(la, lb, smem, (ntok + BK - 1) / BK, acc, wm * 128, nrow);
 
   // fp32 read-modify-write, 4 consecutive columns (16 bytes) per access,

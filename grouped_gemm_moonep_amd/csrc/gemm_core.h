@@ -407,17 +407,38 @@ __device__ __forceinline__ void kstep(const TA& la, const TB& lb, const Ring& ri
   }
 }
 
-// The K loop shared by every GEMM here.  The prologue loads B(0), A(0),
-// B(1); each step then loads A(j+1) and B(j+2) (out-of-range offsets past
-// the last step: they read nothing and keep the wait counts fixed).
+template <int MI>
+__device__ __forceinline__ void zero_acc(f32x16 acc[MI][4]) {
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+}
+
+// The K loop shared by every GEMM here; it sets acc to the product.  The
+// prologue loads B(0), A(0), B(1); each step then loads A(j+1) and B(j+2)
+// (out-of-range offsets past the last step: they read nothing and keep the
+// wait counts fixed).
 template <int MI, class TA, class TB>
 __device__ __forceinline__ void gemm_loop(const TA& la, const TB& lb, const Ring& ring, int nk,
                                           f32x16 acc[MI][4], int arow0, const int nrow[4]) {
   static_assert(TB::kLoads == kLoadsPerStep, "the barrier wait counts B loads");
-  if (nk <= 0) return;
+  if (nk <= 0) {
+    zero_acc<MI>(acc);
+    return;
+  }
   lb.issue(ring.b<0>(), 0, true);
   la.issue(ring.a<0>(), 0, true);
   lb.issue(ring.b<1>(), BK, 1 < nk);
+  // the accumulators are cleared while the first tiles are in flight (after
+  // the wait they would hold the matrix unit back by ~1k cycles per tile)
+  zero_acc<MI>(acc);
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));   // cleared here, not later
   wait_loads<kLoadsPerStep>();
   barrier_reads_done();
   Frags<MI> f0, f1;
@@ -436,15 +457,6 @@ __device__ __forceinline__ void gemm_loop(const TA& la, const TB& lb, const Ring
   __syncthreads();
 }
 
-template <int MI>
-__device__ __forceinline__ void zero_acc(f32x16 acc[MI][4]) {
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-}
 
 // Column (within the 32x32 block) of accumulator elements 4q..4q+3 of this
 // lane (the first of four consecutive columns).
@@ -533,15 +545,31 @@ __device__ __forceinline__ const uint16_t* weight_row(const FfnArgs& a, int p, i
 // have one duration whatever the ranks' tile counts.  Splitting the grid's
 // padded upper bound instead would give the empty tail of each rank's range
 // to whole XCDs (one rank launched alone kept only five of the eight busy).
-// The rank counts are read with uniform loads, which the scalar cache serves
-// (a per-lane load and scan measurably delayed every workgroup's start).
+//
+// The decode takes two rounds of loads, one value per lane in each: the
+// launched ranks' tile counts (one rank per lane, prefix sums by lane
+// shuffles, the rank by a ballot), then a window of 16 tile entries around
+// the one the workgroup index names, which holds both that entry's group and
+// the tile the workgroup takes (groups have at most 8 tiles).  Loading them
+// one dependent scalar load after another took ≈5k cycles per workgroup.
+static_assert(kGroupMax <= 8, "the decode window holds a group on either side of its entry");
 __device__ __forceinline__ bool decode(const FfnArgs& a, int* d, Tile* tl, int* nt) {
-  int64_t nf = 0, ns = 0;
-  for (int i = 0; i < a.nranks; ++i) {
-    const int f = a.nfull[a.rank0 + i];
-    nf += f;
-    ns += a.ntiles[a.rank0 + i] - f;
+  const int lane = threadIdx.x & 63;
+  int f = 0, s = 0;                                    // rank rank0 + lane's full, short tiles
+  if (lane < a.nranks) {
+    f = a.nfull[a.rank0 + lane];
+    s = a.ntiles[a.rank0 + lane] - f;
   }
+  int cf = f, cs = s;                                  // inclusive prefix sums over lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int yf = __shfl_up(cf, o, 64), ys = __shfl_up(cs, o, 64);
+    if (lane >= o) {
+      cf += yf;
+      cs += ys;
+    }
+  }
+  const int64_t nf = __builtin_amdgcn_readlane(cf, 63), ns = __builtin_amdgcn_readlane(cs, 63);
   const int64_t F = nf * a.ntn, Sx = ns * a.ntn;        // full and short workgroups
   const int64_t pf = (F + kXcds - 1) / kXcds, ps = (Sx + kXcds - 1) / kXcds;
   const int64_t x = blockIdx.x % kXcds, c = blockIdx.x / kXcds;
@@ -555,28 +583,28 @@ __device__ __forceinline__ bool decode(const FfnArgs& a, int* d, Tile* tl, int* 
     lt = x * ps + (c - nfx);
     if (c - nfx >= ps || lt >= Sx) return false;
   }
-  // the rank: count of this part's tiles in the ranks before it
-  int r = 0;
-  int64_t first = 0;
-  for (; r < a.nranks - 1; ++r) {                      // lt lies in the part: the last rank ends it
-    const int f = a.nfull[a.rank0 + r];
-    const int n = full ? f : a.ntiles[a.rank0 + r] - f;
-    if ((first + n) * a.ntn > lt) break;
-    first += n;
-  }
+  // the rank: the first lane whose inclusive count of this part's tiles covers lt (lanes past
+  // the launched ranks hold the total, which does)
+  const int cpart = full ? cf : cs;
+  const uint64_t hit = __ballot((int64_t)cpart * a.ntn > lt);
+  const int r = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+  const int64_t first = r > 0 ? __builtin_amdgcn_readlane(cpart, r - 1) : 0;
   *d = a.rank0 + r;
-  if (!full) lt += (int64_t)a.nfull[*d] * a.ntn;       // the rank's short tiles follow its full ones
-  const int l = (int)(lt - (int64_t)first * a.ntn);
+  if (!full) lt += (int64_t)__builtin_amdgcn_readlane(f, r) * a.ntn;   // short tiles follow full
+  const int l = (int)(lt - first * a.ntn);
   const int tp = l / a.ntn;
   const int32_t* base = a.tiles + (int64_t)*d * a.max_tiles * 4;
-  const int grp = base[tp * 4 + 3];
+  const int w0 = tp - 7 < 0 ? 0 : tp - 7;              // window: entries w0 .. w0 + 15
+  const int ei = w0 * 4 + lane;
+  const int v = ei < a.max_tiles * 4 ? base[ei] : 0;
+  const int grp = __builtin_amdgcn_readlane(v, (tp - w0) * 4 + 3);
   const int gs = grp >> 4, gm = grp & 15;
   const int rem = l - gs * a.ntn;
   *nt = rem / gm;
-  const int32_t* e = base + (gs + rem % gm) * 4;
-  tl->row = e[0];
-  tl->m0 = e[1];
-  tl->m1 = e[2];
+  const int k = (gs + rem % gm - w0) * 4;
+  tl->row = __builtin_amdgcn_readlane(v, k);
+  tl->m0 = __builtin_amdgcn_readlane(v, k + 1);
+  tl->m1 = __builtin_amdgcn_readlane(v, k + 2);
   return true;
 }
 
