@@ -69,12 +69,6 @@ typedef __attribute__((address_space(3))) char lds_t;
 
 __device__ __forceinline__ int round_up(int n, int m) { return (n + m - 1) / m * m; }
 
-// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ unsigned bf16_rne(float f) {
-  const unsigned u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // ---------------------------------------------------------------------------
@@ -462,8 +456,14 @@ __device__ __forceinline__ void gemm_loop(const TA& la, const TB& lb, const Ring
 // lane (the first of four consecutive columns).
 __device__ __forceinline__ int acc_col(int q, int lh) { return 8 * q + 4 * lh; }
 
+// Two fp32 -> two bf16 (lo in bits 0-15), round to nearest, ties to even, by
+// the gfx950 packed conversion (one instruction; a shift-and-add rounding
+// took about 9 vector instructions per pair, which the epilogues issue with
+// the matrix unit idle).
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // Epilogue staging: a wave's bf16 output sub-tile (ROWS x NC columns) is
@@ -550,8 +550,8 @@ __device__ __forceinline__ const uint16_t* weight_row(const FfnArgs& a, int p, i
 // launched ranks' tile counts (one rank per lane, prefix sums by lane
 // shuffles, the rank by a ballot), then a window of 16 tile entries around
 // the one the workgroup index names, which holds both that entry's group and
-// the tile the workgroup takes (groups have at most 8 tiles).  Loading them
-// one dependent scalar load after another took ≈5k cycles per workgroup.
+// the tile the workgroup takes (groups have at most 8 tiles), in place of a
+// chain of dependent scalar loads.
 static_assert(kGroupMax <= 8, "the decode window holds a group on either side of its entry");
 __device__ __forceinline__ bool decode(const FfnArgs& a, int* d, Tile* tl, int* nt) {
   const int lane = threadIdx.x & 63;

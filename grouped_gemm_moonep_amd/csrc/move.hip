@@ -36,10 +36,12 @@ __device__ __forceinline__ int round_up(int n, int m) { return (n + m - 1) / m *
 __device__ __forceinline__ float bf16_lo(unsigned v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned v) { return __uint_as_float(v & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ unsigned bf16_rne(float f) {
-  const unsigned u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two fp32 -> two bf16 (lo in bits 0-15), round to nearest, ties to even (the
+// gfx950 packed conversion).
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
       if (v < a.nv) {
         u32x4 o;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = bf16_rne(acc[u][2 * j]) | (bf16_rne(acc[u][2 * j + 1]) << 16);
+        for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(acc[u][2 * j], acc[u][2 * j + 1]);
         __builtin_nontemporal_store(o, dst + v);
       }
     }
