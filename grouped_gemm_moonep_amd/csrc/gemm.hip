@@ -34,7 +34,6 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, const Ring& smem, 
   // wave's 32 MI x 64 block of Z is staged in LDS and stored as whole rows.
   // Rows past the segment fall outside the store range; columns past H' get
   // an out-of-range offset.
-  const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
   typedef Stage<32 * MI, 64> St;
   lds_t* reg = smem.base + wave * St::kBytes;
 #pragma unroll
@@ -52,7 +51,7 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, const Ring& smem, 
           // sequence: the epilogue runs with the matrix unit idle
           z[e] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
         }
-        St::put(reg, i * 32 + lr, j * 32 + acc_col(q, lh), pack_bf16x2(z[0], z[1]),
+        St::put(reg, i, j, q, pack_bf16x2(z[0], z[1]),
                 pack_bf16x2(z[2], z[3]));
       }
   const Rsrc zs = make_rsrc(a.z + ((int64_t)d * a.NvS + tl.m0) * a.Hp + n0,
@@ -77,7 +76,6 @@ __device__ __forceinline__ void down_tile(const FfnArgs& a, const Ring& smem, in
   f32x16 acc[MI][4];
   gemm_loop<MI>(la, lb, smem, a.Hp / BK, acc, wm * 32 * MI, nrow);
 
-  const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
   typedef Stage<32 * MI, 128> St;
   lds_t* reg = smem.base + wave * St::kBytes;
 #pragma unroll
@@ -86,7 +84,7 @@ __device__ __forceinline__ void down_tile(const FfnArgs& a, const Ring& smem, in
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        St::put(reg, i * 32 + lr, j * 32 + acc_col(q, lh),
+        St::put(reg, i, j, q,
                 pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                 pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
   const Rsrc ys = make_rsrc(a.y + ((int64_t)d * a.NvS + tl.m0) * a.H + n0,

@@ -35,7 +35,6 @@ __device__ __forceinline__ void bwd_dz_tile(const FfnArgs& a, const Ring& smem, 
   f32x16 acc[MI][4];
   gemm_loop<MI>(la, lb, smem, a.H / BK, acc, wm * 32 * MI, nrow);
 
-  const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
   typedef Stage<32 * MI, 128> St;
   lds_t* reg = smem.base + wave * St::kBytes;
 #pragma unroll
@@ -44,7 +43,7 @@ __device__ __forceinline__ void bwd_dz_tile(const FfnArgs& a, const Ring& smem, 
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        St::put(reg, i * 32 + lr, j * 32 + acc_col(q, lh),
+        St::put(reg, i, j, q,
                 pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                 pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
   const Rsrc ds = make_rsrc(a.dz + ((int64_t)d * a.NvS + tl.m0) * a.Hp + n0,
@@ -107,9 +106,9 @@ __device__ __forceinline__ void bwd_gu_tile(const FfnArgs& a, const Ring& smem, 
           du[e] = dz * (g * sg);
           dg[e] = dz * u * (sg * (1.0f + g * (1.0f - sg)));
         }
-        St::put(reg_g, i * 32 + lr, j * 32 + acc_col(q, lh), pack_bf16x2(dg[0], dg[1]),
+        St::put(reg_g, i, j, q, pack_bf16x2(dg[0], dg[1]),
                 pack_bf16x2(dg[2], dg[3]));
-        St::put(reg_u, i * 32 + lr, j * 32 + acc_col(q, lh), pack_bf16x2(du[0], du[1]),
+        St::put(reg_u, i, j, q, pack_bf16x2(du[0], du[1]),
                 pack_bf16x2(du[2], du[3]));
       }
   const int64_t base = ((int64_t)d * a.NvS + tl.m0) * a.Hp + n0;
@@ -138,7 +137,6 @@ __device__ __forceinline__ void bwd_dx_tile(const FfnArgs& a, const Ring& smem, 
   f32x16 acc[MI][4];
   gemm_loop<MI>(la, lb, smem, 2 * a.Hp / BK, acc, wm * 32 * MI, nrow);
 
-  const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
   typedef Stage<32 * MI, 128> St;
   lds_t* reg = smem.base + wave * St::kBytes;
 #pragma unroll
@@ -147,7 +145,7 @@ __device__ __forceinline__ void bwd_dx_tile(const FfnArgs& a, const Ring& smem, 
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        St::put(reg, i * 32 + lr, j * 32 + acc_col(q, lh),
+        St::put(reg, i, j, q,
                 pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                 pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
   const Rsrc xs = make_rsrc(a.dx + ((int64_t)d * a.NvS + tl.m0) * a.H + n0,

@@ -471,12 +471,22 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 // layout), then read back 16 bytes per lane along whole rows and stored with
 // 16-byte buffer stores, so every store instruction writes complete rows.
 template <int ROWS, int NC>
+// The padded row stride is 4 banks (mod 64) for NC = 128, so the 32 rows of a
+// put instruction would meet two to a bank; rows 16..31 of every 32 keep the
+// two 8-byte halves of each 16-byte chunk swapped, which puts them on the
+// other two banks of each group of four (the flush swaps them back).
 struct Stage {
   static constexpr int kRowBytes = NC * 2 + 16;     // padded row (16-byte aligned)
   static constexpr int kBytes = ROWS * kRowBytes;
-  __device__ __forceinline__ static void put(lds_t* reg, int row, int col, unsigned lo, unsigned hi) {
+  // this lane's accumulator piece (i, j, q) as bf16 pairs lo, hi: row 32 i + lane%32, columns
+  // 32 j + 8 q + 4 (lane/32) .. +3 (the layout mma1 leaves)
+  __device__ __forceinline__ static void put(lds_t* reg, int i, int j, int q, unsigned lo,
+                                             unsigned hi) {
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    *(__attribute__((address_space(3))) u32x2*)(reg + row * kRowBytes + col * 2) = u32x2{lo, hi};
+    const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
+    const int lane_off = lr * kRowBytes + 8 * (lh ^ ((lr >> 4) & 1));
+    const int off = lane_off + 32 * i * kRowBytes + 64 * j + 16 * q;
+    *(__attribute__((address_space(3))) u32x2*)(reg + off) = u32x2{lo, hi};
   }
   // store the staged sub-tile: rows [0,ROWS) to row m0 + r of `dst` (row
   // stride ld elements, rows past the descriptor range dropped), columns
@@ -484,13 +494,15 @@ struct Stage {
   __device__ __forceinline__ static void flush(const lds_t* reg, Rsrc dst, int m0, int64_t ld,
                                                int c0, int cols_valid) {
     constexpr int kLanesPerRow = NC / 8, kRowsPerInst = 64 / kLanesPerRow;
+    static_assert(16 % kRowsPerInst == 0, "an instruction's rows share the swap of their 16");
     const int lane = threadIdx.x & 63;
     const int r0 = lane / kLanesPerRow, ch = lane % kLanesPerRow;
     const int col = c0 + ch * 8;
 #pragma unroll
     for (int t = 0; t < ROWS / kRowsPerInst; ++t) {
       const int r = t * kRowsPerInst + r0;
-      const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(reg + r * kRowBytes + ch * 16);
+      u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(reg + r * kRowBytes + ch * 16);
+      if ((((t * kRowsPerInst) >> 4) & 1) != 0) v = __builtin_shufflevector(v, v, 2, 3, 0, 1);
       const uint32_t off = col < cols_valid ? (uint32_t)(((int64_t)(m0 + r) * ld + col) * 2) : kOob;
       __builtin_amdgcn_raw_buffer_store_b128(v, dst, off, 0, 0);
     }
