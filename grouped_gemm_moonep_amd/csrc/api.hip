@@ -193,6 +193,9 @@ moonep_status_t moonep_create(const moonep_config_t* cfg, moonep_handle_t* out) 
       {&c.line, d.E},
       {&c.chunk_err, (int64_t)d.R * d.nch},
       {&c.efix, 2LL * d.E},
+      {&c.aend, 2LL * d.E},
+      {&c.an, 2LL * d.E},
+      {&c.rend, d.R},
   };
   for (auto& a : allocs) {
     if (hipMalloc((void**)a.p, (size_t)a.n * sizeof(int32_t)) != hipSuccess) {
@@ -208,7 +211,7 @@ moonep_status_t moonep_destroy(moonep_handle_t h) {
   if (!h) return MOONEP_OK;
   Ctx& c = h->c;
   int32_t* ptrs[] = {c.cc, c.shift, c.pieces, c.npieces, c.line,
-                     c.chunk_err, c.efix};
+                     c.chunk_err, c.efix, c.aend, c.an, c.rend};
   hipError_t err = hipSuccess;
   for (int32_t* p : ptrs)
     if (p) {

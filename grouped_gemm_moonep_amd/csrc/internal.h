@@ -46,7 +46,7 @@ struct Ctx {
   int device;
   int num_cu_device;
   // planning scratch (device)
-  int32_t* cc;        // [R][nch][E] chunk counts, then line-position bases
+  int32_t* cc;        // [R][nch][E] expert counts of each planning chunk
   int32_t* shift;     // [R][E] slot - line position for (d, e)
   int32_t* pieces;    // [R groups][R+1][2] (hi, rank) of each line piece
   int32_t* npieces;   // [R]
@@ -54,6 +54,9 @@ struct Ctx {
   int32_t* chunk_err; // [R][nch] routing error bits found per chunk
   int32_t* efix;      // [E][2] (rank, slot - line position) of an expert whose tokens all
                       // go to one rank, rank -1 for an expert split over ranks
+  int32_t* aend;      // [R][2E/R] padded end slot of each rank's active row q
+  int32_t* an;        // [R][2E/R] real tokens of each rank's active row q
+  int32_t* rend;      // [R] end of each rank's last segment (its used slots)
 };
 
 bool dims_from_config(const moonep_config_t* cfg, Dims* out);

@@ -22,14 +22,18 @@
 //   plan_hist   (R x chunks workgroups): per-chunk expert counts from 64-bit
 //                LDS lane masks (order-independent), routing validation;
 //   plan_solve  (one workgroup of 1024 threads): counts, loads, lines, the
-//                serial chain-greedy (at most 2R steps), rows, cu_seqlens,
-//                prefetch and reduce tables, per-chunk line bases;
+//                serial chain-greedy (at most 2R steps), each rank's active
+//                rows with their padded ends, prefetch slots;
 //   plan_assign (R x chunks workgroups): stable rank of each token among the
 //                earlier tokens of the same expert (popcount of the lane
-//                masks below it), its line position, piece, row and slot;
-//                padding slots get src = -1.  One more workgroup per rank
-//                builds that rank's grouped-GEMM tile schedule
-//                (tile_schedule.h) at the same time.
+//                masks below it), its line position (the chunk's base summed
+//                from the earlier chunks' counts), piece, row and slot;
+//                padding slots get src = -1.  At the same time one more
+//                workgroup per rank writes that rank's cu_seqlens and
+//                seg_tokens and builds its grouped-GEMM tile schedule
+//                (tile_schedule.h), and one more the reduce_grad tables:
+//                work that only reads the solve's results, kept off its
+//                single workgroup.
 #include "internal.h"
 #include "tile_schedule.h"
 
@@ -50,6 +54,9 @@ struct PlanArgs {
   int32_t* npieces;
   int32_t* line;
   int32_t* efix;
+  int32_t* aend;      // [R][2L] padded end slot of each rank's active row q
+  int32_t* an;        // [R][2L] real tokens of each rank's active row q
+  int32_t* rend;      // [R] end of each rank's last segment (its used slots)
   int32_t* counts;
   int32_t* dest;
   int32_t* src;
@@ -160,9 +167,8 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   __shared__ int don_g[kMaxR + 1], don_r[kMaxR + 1], don_amt[kMaxR + 1];
   __shared__ int recv_g[kMaxR], recv_lo[kMaxR], recv_hi[kMaxR];
   __shared__ int ent_n[2 * kMaxE], ent_lo[2 * kMaxE], ent_row[2 * kMaxE];
-  __shared__ int act_row[2 * kMaxE], act_end[2 * kMaxE], act_n[2 * kMaxE];
+  __shared__ int act_row[2 * kMaxE];
   __shared__ int nact[kMaxR], nrem[kMaxR], npf[kMaxR], pfpre[kMaxR];
-  __shared__ int hcount[kMaxE];
   __shared__ int ord_len[3 * kMaxE], ord_ent[3 * kMaxE], ord_cnt[3 * kMaxE];  // phase F
   __shared__ int scan_scratch[4 * kSolveWaves];
   __shared__ int s_err, s_maxload, s_ndon, s_dups, s_pad, s_nd, s_nq;
@@ -177,10 +183,11 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   for (int e = tid; e < E; e += kSolveThreads) T[e] = 0;
   __syncthreads();
 
-  // Phase A: counts per (r, e), the exclusive per-chunk prefix (in place) and
-  // the expert loads T_e (an order-independent integer sum in LDS).  Two
-  // (r, e) columns per pass with all their chunk loads in flight together,
-  // and the per-chunk error bits loaded beside them.
+  // Phase A: counts per (r, e) summed over the chunks and the expert loads
+  // T_e (an order-independent integer sum in LDS).  Two (r, e) columns per
+  // pass with all their chunk loads in flight together, and the per-chunk
+  // error bits loaded beside them.  (Each plan_assign workgroup sums the
+  // chunks before its own, so nothing is written back here.)
   {
     constexpr int kBatch = 8;            // chunk loads per column in flight
     int cerr = 0;
@@ -188,8 +195,8 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     for (int i0 = tid; i0 < RE; i0 += 2 * kSolveThreads) {
       const int i1 = i0 + kSolveThreads;
       const bool has1 = i1 < RE;
-      int32_t* col0 = a.cc + (int64_t)(i0 / E) * nch * E + (i0 % E);
-      int32_t* col1 = has1 ? a.cc + (int64_t)(i1 / E) * nch * E + (i1 % E) : col0;
+      const int32_t* col0 = a.cc + (int64_t)(i0 / E) * nch * E + (i0 % E);
+      const int32_t* col1 = has1 ? a.cc + (int64_t)(i1 / E) * nch * E + (i1 % E) : col0;
       int run0 = 0, run1 = 0;
       for (int ch0 = 0; ch0 < nch; ch0 += kBatch) {
         int v0[kBatch], v1[kBatch];
@@ -200,15 +207,10 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
           v1[u] = ok && has1 ? col1[(int64_t)(ch0 + u) * E] : 0;
         }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-          if (ch0 + u < nch) {
-            col0[(int64_t)(ch0 + u) * E] = run0;
-            run0 += v0[u];
-            if (has1) {
-              col1[(int64_t)(ch0 + u) * E] = run1;
-              run1 += v1[u];
-            }
-          }
+        for (int u = 0; u < kBatch; ++u) {
+          run0 += v0[u];
+          run1 += v1[u];
+        }
       }
       a.counts[i0] = run0;
       atomicAdd(&T[i0 % E], run0);
@@ -230,6 +232,10 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     for (int i = tid; i < R * (E + B); i += kSolveThreads) { a.cu[i] = 0; a.segn[i] = 0; }
     for (int i = tid; i < R * B; i += kSolveThreads) a.pf[i] = -1;
     for (int i = tid; i < 2 * E; i += kSolveThreads) a.aux[a.ax.act + i] = -1;
+    for (int d = tid; d < R; d += kSolveThreads) {
+      a.aux[a.ax.nact + d] = 0;
+      a.rend[d] = 0;
+    }
     if (tid == 0) {
       a.aux[a.ax.pf_n] = 0;
       a.aux[a.ax.dup_n] = 0;
@@ -311,57 +317,91 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    const int nd = s_nd;
-    int qt = s_nq;
-    int qh = 0;
-    int ndon = 0;
-    int i = 0;
-    int x = nd ? X[donors[0]] : 0;
-    int bad = 0;
-    while (qh < qt && !bad) {
-      const int r = queue[qh++];
-      const int dn = need[r];
+  // The chain-greedy itself, on wave 0 with its state in registers: lane j
+  // holds queue entry j, donor j (by position) and its excess, group j's
+  // need, keep and donation count, and donation j once made; every step reads
+  // and writes single lanes (readlane, a lane select) instead of LDS, whose
+  // latency made up the loop's time.  The queue never exceeds R entries (the
+  // initial receivers plus each donor at most once) and there are at most R
+  // donations, so one lane each suffices (R <= 64).  A donor's donations are
+  // consecutive, so each starts at the donor's final keep plus what the donor
+  // gave before it.
+  if (tid < 64) {
+    const int lane = tid;
+    // lane `at` of v becomes val (at is wave-uniform)
+    auto writelane = [lane](int val, int at, int v) { return lane == at ? val : v; };
+    const int nd = s_nd, nq = s_nq;
+    int qv = lane < nq ? queue[lane] : 0;
+    const int dv = lane < nd ? donors[lane] : 0;
+    const int dx = lane < nd ? X[dv] : 0;
+    int needv = lane < R ? need[lane] : 0;
+    int keepv = lane < R ? keep[lane] : 0;
+    int cntv = 0;
+    int dong = 0, donr = 0, dona = 0, donc = 0, donk = 0;
+    int qt = nq, qh = 0, ndon = 0, i = 0, given = 0, k = 0, bad = 0;
+    int x = nd ? __builtin_amdgcn_readlane(dx, 0) : 0;
+    while (qh < qt) {
+      const int r = __builtin_amdgcn_readlane(qv, qh);
+      ++qh;
+      const int dn = __builtin_amdgcn_readlane(needv, r);
       if (i >= nd || ndon >= R) { bad = 1; break; }
-      const int g = donors[i];
-      don_g[ndon] = g; don_r[ndon] = r; don_amt[ndon] = dn; ++ndon;
+      const int g = __builtin_amdgcn_readlane(dv, i);
+      dong = writelane(g, ndon, dong);
+      donr = writelane(r, ndon, donr);
+      dona = writelane(dn, ndon, dona);
+      donc = writelane(given, ndon, donc);
+      donk = writelane(k, ndon, donk);
+      cntv = writelane(k + 1, g, cntv);
+      ++ndon;
+      given += dn;
+      ++k;
       if (dn <= x) {
         x -= dn;
-        if (x == 0 && i + 1 < nd) { ++i; x = X[donors[i]]; }
+        if (x == 0 && i + 1 < nd) {
+          ++i;
+          x = __builtin_amdgcn_readlane(dx, i);
+          given = 0;
+          k = 0;
+        }
       } else {
         const int sh = dn - x;
-        keep[g] -= sh;
-        need[g] = sh;
-        if (qt >= 2 * kMaxR + 2) { bad = 1; break; }
-        queue[qt++] = g;
+        keepv = writelane(__builtin_amdgcn_readlane(keepv, g) - sh, g, keepv);
+        needv = writelane(sh, g, needv);
+        if (qt >= 64) { bad = 1; break; }
+        qv = writelane(g, qt, qv);
+        ++qt;
         ++i;
-        x = i < nd ? X[donors[i]] : 0;
+        x = i < nd ? __builtin_amdgcn_readlane(dx, i) : 0;
+        given = 0;
+        k = 0;
       }
     }
-    s_ndon = ndon;
-    if (bad) s_err = 8;   // internal: inconsistent counts (cannot happen)
-  }
-  __syncthreads();
-  // pieces of every group's line: [0, keep) to the home rank, then the
-  // group's donations in emission order
-  const int ndon_all = s_ndon;
-  for (int g = tid; g < R; g += kSolveThreads) {
-    int np = 0, lo = 0;
-    int32_t* pg = a.pieces + (int64_t)g * (R + 1) * 2;
-    if (keep[g] > 0) {
-      lo = keep[g];
-      pg[0] = lo; pg[1] = g; np = 1;
+    // pieces of every group's line: [0, keep) to the home rank, then the
+    // group's donations in emission order
+    const int kg = __shfl(keepv, dong, 64);              // final keep of donation lane's donor
+    if (lane < ndon) {
+      const int lo = kg + donc, hi = lo + dona;
+      int32_t* pg = a.pieces + (int64_t)dong * (R + 1) * 2;
+      const int pi = (kg > 0 ? 1 : 0) + donk;
+      pg[2 * pi] = hi;
+      pg[2 * pi + 1] = donr;
+      recv_g[donr] = dong;        // each rank receives from at most one group
+      recv_lo[donr] = lo;
+      recv_hi[donr] = hi;
     }
-    for (int q = 0; q < ndon_all; ++q) {
-      if (don_g[q] != g) continue;
-      const int dlo = lo;
-      lo += don_amt[q];
-      pg[2 * np] = lo; pg[2 * np + 1] = don_r[q]; ++np;
-      recv_g[don_r[q]] = g;        // each rank receives from at most one group
-      recv_lo[don_r[q]] = dlo;
-      recv_hi[don_r[q]] = lo;
+    if (lane < R) {
+      int32_t* pg = a.pieces + (int64_t)lane * (R + 1) * 2;
+      if (keepv > 0) {
+        pg[0] = keepv;
+        pg[1] = lane;
+      }
+      a.npieces[lane] = (keepv > 0 ? 1 : 0) + cntv;
+      keep[lane] = keepv;
     }
-    a.npieces[g] = np;
+    if (lane == 0) {
+      s_ndon = ndon;
+      if (bad) s_err = 8;   // internal: inconsistent counts (cannot happen)
+    }
   }
   __syncthreads();
 
@@ -459,13 +499,13 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     }
   }
   __syncthreads();
-  int tot_cnt;
+  int tot_cnt, tot_len;
   {
     const int per = (nslot + kSolveThreads - 1) / kSolveThreads;
     const int b0 = min(nslot, tid * per), b1 = min(nslot, b0 + per);
     int sl = 0, sc = 0;
     for (int i = b0; i < b1; ++i) { sl += ord_len[i]; sc += ord_ent[i] >= 0; }
-    int pl, pc, tot_len;
+    int pl, pc;
     block_scan2(sl, sc, &pl, &pc, &tot_len, &tot_cnt, scan_scratch);
     for (int i = b0; i < b1; ++i) {          // exclusive prefixes, in place
       const int l = ord_len[i];
@@ -495,8 +535,8 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
       a.efix[2 * e] = n == T[e] ? d : -1;
       if (n == T[e]) a.efix[2 * e + 1] = start - ent_lo[idx];
       act_row[d * L2 + q] = row;
-      act_end[d * L2 + q] = start + len;
-      act_n[d * L2 + q] = n;
+      a.aend[d * L2 + q] = start + len;
+      a.an[d * L2 + q] = n;
       if (row >= E) a.pf[d * B + (row - E)] = e;
       pad += len - n;
     }
@@ -508,6 +548,8 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     const int next = d + 1 < R ? ord_cnt[(d + 1) * S3] : tot_cnt;
     nact[d] = next - ord_cnt[d * S3];
     a.aux[a.ax.nact + d] = nact[d];
+    // the rank's segments lie back to back from slot 0
+    a.rend[d] = (d + 1 < R ? ord_len[(d + 1) * S3] : tot_len) - ord_len[d * S3];
     const int rem = nrem[d];
     a.stats[MOONEP_STAT_REMOTE_GROUP + d] = rem ? recv_g[d] : -1;
     a.stats[MOONEP_STAT_REMOTE_GROUP + R + d] = rem;
@@ -522,61 +564,9 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   for (int i = tid; i < R * L2; i += kSolveThreads) {
     const int d = i / L2, q = i - (i / L2) * L2;
     a.aux[a.ax.act + i] = q < nact[d] ? act_row[i] : -1;
+    if (q >= nact[d]) a.an[i] = 0;              // entries past the active rows hold no tokens
   }
   if (tid == 0) a.aux[a.ax.pf_n] = R > 0 ? pfpre[R - 1] + npf[R - 1] : 0;
-
-  // Phase G: cu_seqlens and seg_tokens for every (rank, row).
-  const int EB = E + B;
-  // The rank's active rows are in ascending row order: binary search for
-  // the last one at or below `row`.
-  for (int idx = tid; idx < R * EB; idx += kSolveThreads) {
-    const int d = idx / EB, row = idx - (idx / EB) * EB;
-    const int* ar = act_row + d * L2;
-    int lo = 0, hi = nact[d];          // first q with ar[q] > row lies in [lo, hi]
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (ar[mid] <= row) lo = mid + 1;
-      else hi = mid;
-    }
-    int end = 0, n = 0;
-    if (lo > 0) {
-      end = act_end[d * L2 + lo - 1];
-      if (ar[lo - 1] == row) n = act_n[d * L2 + lo - 1];
-    }
-    a.cu[idx] = end;
-    a.segn[idx] = n;
-  }
-
-  // Phase G3: holders of every home expert that has prefetch copies, in
-  // ascending rank (the reduce_grad order).
-  for (int e = tid; e < E; e += kSolveThreads) {
-    const int g = e / L, i = e - g * L;
-    int cnt = 0;
-#pragma unroll 8
-    for (int d = 0; d < R; ++d) cnt += (recv_g[d] == g && ent_row[d * L2 + L + i] >= E) ? 1 : 0;
-    hcount[e] = cnt;
-  }
-  __syncthreads();
-  {
-    const int e = tid;
-    const int has = (e < E && hcount[e] > 0) ? 1 : 0;
-    const int cnt = e < E ? hcount[e] : 0;
-    int q, first, nexp, nhold;
-    block_scan2(has, cnt, &q, &first, &nexp, &nhold, scan_scratch);
-    if (has) {
-      const int g = e / L, i = e - g * L;
-      a.aux[a.ax.dup_e + q] = e;
-      a.aux[a.ax.dup_first + q] = first;
-      a.aux[a.ax.dup_cnt + q] = cnt;
-      int k = 0;
-#pragma unroll 8
-      for (int d = 0; d < R; ++d) {
-        const int row = ent_row[d * L2 + L + i];
-        if (recv_g[d] == g && row >= E) a.aux[a.ax.hold + first + k++] = d * B + (row - E);
-      }
-    }
-    if (tid == 0) a.aux[a.ax.dup_n] = nexp;
-  }
 
   if (tid == 0) {
     a.stats[MOONEP_STAT_ERROR] = s_err;
@@ -598,14 +588,105 @@ constexpr int kShiftLds = 4096;     // shift table staged in LDS up to R*E ints
 constexpr int kPiecesLds = 1024;    // piece table staged in LDS up to this many ints
 
 __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
+  const int tid = threadIdx.x;
+  const int L2 = 2 * a.L, EB = a.E + a.B;
   if (blockIdx.x == a.nch) {
-    // the grid's extra column: rank blockIdx.y's grouped-GEMM tile schedule,
-    // built from plan_solve's segments alongside the token assignment
+    // the grid's first extra column: rank d's cu_seqlens and seg_tokens, then its
+    // grouped-GEMM tile schedule, both from plan_solve's active rows, alongside the
+    // token assignment
+    __shared__ int s_act[2 * kMaxE], s_aend[2 * kMaxE], s_an[2 * kMaxE];
     __shared__ int wsum[4];
     __shared__ TileSchedLds sl;
-    build_tile_schedule(a.aux + a.ax.act, a.cu, a.segn, a.aux + a.ax.tiles,
-                        a.aux + a.ax.ntiles, a.aux + a.ax.nfull, blockIdx.y, 2 * a.L,
-                        a.E + a.B, a.tp, a.max_tiles, wsum, sl);
+    const int d = blockIdx.y;
+    if (a.stats[MOONEP_STAT_ERROR] == 0) {     // (a failed plan has its zeros already)
+      const int na = a.aux[a.ax.nact + d];
+      for (int q = tid; q < na; q += kPlanChunk) {
+        s_act[q] = a.aux[a.ax.act + d * L2 + q];
+        s_aend[q] = a.aend[d * L2 + q];
+        s_an[q] = a.an[d * L2 + q];
+      }
+      __syncthreads();
+      // each row's entry: the end of the last active row at or below it (the rows are
+      // ascending), its token count if it is active itself
+      for (int row = tid; row < EB; row += kPlanChunk) {
+        int lo = 0, hi = na;                   // first q with s_act[q] > row lies in [lo, hi]
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s_act[mid] <= row) lo = mid + 1;
+          else hi = mid;
+        }
+        a.cu[d * EB + row] = lo > 0 ? s_aend[lo - 1] : 0;
+        a.segn[d * EB + row] = lo > 0 && s_act[lo - 1] == row ? s_an[lo - 1] : 0;
+      }
+    }
+    build_tile_schedule(a.aux + a.ax.act, a.aend, a.an, a.aux + a.ax.tiles,
+                        a.aux + a.ax.ntiles, a.aux + a.ax.nfull, d, L2, a.tp, a.max_tiles,
+                        wsum, sl);
+    return;
+  }
+  if (blockIdx.x == a.nch + 1) {
+    // the second extra column (one workgroup): the reduce_grad tables.  The home
+    // experts that have prefetch copies (ascending), the first holder of each and
+    // their count, and the holder slots d B + j of each expert in ascending rank.
+    // Rank d holds expert e in slot j iff prefetch_src[d B + j] = e, at most once.
+    if (blockIdx.y != 0 || a.stats[MOONEP_STAT_ERROR] != 0) return;
+    __shared__ int hcnt[kMaxE], hfirst[kMaxE];
+    __shared__ unsigned long long hmask[kMaxE];
+    __shared__ int wsum[4];
+    const int E = a.E, RB = a.R * a.B;
+    for (int e = tid; e < E; e += kPlanChunk) {
+      hcnt[e] = 0;
+      hmask[e] = 0ull;
+    }
+    constexpr int kPer = kMaxE / kPlanChunk;   // R B <= E <= kMaxE slots, kPer per thread
+    int pe[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + u * kPlanChunk;
+      pe[u] = i < RB ? a.pf[i] : -1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (pe[u] >= 0) {
+        const int d = (tid + u * kPlanChunk) / a.B;
+        atomicAdd(&hcnt[pe[u]], 1);
+        atomicOr(&hmask[pe[u]], 1ull << d);
+      }
+    __syncthreads();
+    // one exclusive scan over the experts (kPer consecutive ones per thread) of
+    // (has copies) in the low 16 bits and (copies) in the high 16 (each total <= E)
+    int v[kPer], sum = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid * kPer + u;
+      const int c = e < E ? hcnt[e] : 0;
+      v[u] = (c > 0 ? 1 : 0) | (c << 16);
+      sum += v[u];
+    }
+    int total;
+    int run = block_scan256(sum, &total, wsum);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid * kPer + u;
+      if (e < E && v[u] != 0) {
+        const int q = run & 0xFFFF, first = run >> 16;
+        a.aux[a.ax.dup_e + q] = e;
+        a.aux[a.ax.dup_first + q] = first;
+        a.aux[a.ax.dup_cnt + q] = v[u] >> 16;
+        hfirst[e] = first;
+      }
+      run += v[u];
+    }
+    if (tid == 0) a.aux[a.ax.dup_n] = total & 0xFFFF;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (pe[u] >= 0) {
+        const int i = tid + u * kPlanChunk, d = i / a.B;
+        const int k = __popcll(hmask[pe[u]] & ((1ull << d) - 1ull));
+        a.aux[a.ax.hold + hfirst[pe[u]] + k] = i;
+      }
     return;
   }
   __shared__ unsigned long long mask[4][kMaxE];
@@ -615,8 +696,7 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
   __shared__ int s_np[kMaxR];
   __shared__ int s_plo[kPlanChunk], s_phi[kPlanChunk];
   __shared__ int s_efix[2 * kMaxE];
-  const int ch = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
-  const int err = a.stats[MOONEP_STAT_ERROR];
+  const int ch = blockIdx.x, r = blockIdx.y;
   const int s = ch * kPlanChunk + tid;
   const int w = tid >> 6, lane = tid & 63;
   const unsigned long long bit = 1ull << lane;
@@ -624,57 +704,125 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
   // the lookup tables of this chunk, staged in LDS when they fit
   const int npc = a.R * (a.R + 1) * 2;
   const bool tab = a.R * a.E <= kShiftLds && npc <= kPiecesLds;
-  if (!err) {
-    for (int i = tid; i < 4 * a.E; i += kPlanChunk) mask[i / a.E][i % a.E] = 0ull;
-    // this token's expert ids, loaded once
-    int ids[kMaxK];
+  // Every global load of the staging is issued before the first value is
+  // used, so the workgroup waits for one round of memory latency (the
+  // tables were written by the previous kernel, possibly on another XCD):
+  // this token's expert ids; the padding of this thread's active row (rows
+  // ch, ch + nch, ... of the rank: thread t takes row ch + t nch, its padded
+  // end and token count; entries past the rank's active rows have no tokens)
+  // and the end of the rank's last segment; for this thread's first expert
+  // the line start, up to 16 earlier chunks and 8 lower ranks (the chunk's
+  // line position of the expert is their sum); the first entries of the
+  // per-expert shortcut, shift and piece tables.  Larger shapes load the
+  // rest in further rounds.  The loads do not wait for the plan's error flag
+  // (they stay in bounds whatever the tables hold).
+  int ids[kMaxK];
+  if ((a.K & 3) == 0 && ((uintptr_t)a.topk & 15) == 0) {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int k = 0; k < kMaxK; k += 4) {
+      i32x4 v = {0, 0, 0, 0};
+      if (s < a.S && k < a.K) v = *(const i32x4*)(a.topk + tok * a.K + k);
+      ids[k] = v[0]; ids[k + 1] = v[1]; ids[k + 2] = v[2]; ids[k + 3] = v[3];
+    }
+  } else {
 #pragma unroll
     for (int k = 0; k < kMaxK; ++k) ids[k] = (s < a.S && k < a.K) ? a.topk[tok * a.K + k] : 0;
-    // the active row whose padding this thread clears (rows ch, ch + nch, ... of the rank:
-    // thread t takes row ch + t nch) and the end of the rank's last segment, loaded up front
-    // so that their latency overlaps the staging below
-    const int L2 = 2 * a.L, EB = a.E + a.B;
-    const int q_pad = ch + tid * a.nch;
-    const int pad_row = q_pad < L2 ? a.aux[a.ax.act + r * L2 + q_pad] : -1;
-    const int last = a.cu[r * EB + EB - 1];
-    // line position of this chunk's first token of expert e: the expert's
-    // line start + tokens of lower ranks + tokens of earlier chunks of rank r
-    const int32_t* gbase = a.cc + ((int64_t)r * a.nch + ch) * a.E;
-    for (int i = tid; i < a.E; i += kPlanChunk) {
-      int v = gbase[i] + a.line[i];
-#pragma unroll 8
-      for (int q = 0; q < r; ++q) v += a.counts[q * a.E + i];
+  }
+  const int q_pad = ch + tid * a.nch;
+  const int pad_end = q_pad < L2 ? a.aend[r * L2 + q_pad] : 0;
+  const int pad_n = q_pad < L2 ? a.an[r * L2 + q_pad] : 0;
+  const int last = a.rend[r];
+  const int RE = a.R * a.E;
+  constexpr int kShiftU = 12;                      // shift entries per thread in the first round
+  constexpr int kEfixU = 4;                        // shortcut entries per thread in the first round
+  const int32_t* col = a.cc + (int64_t)r * a.nch * a.E + tid;      // chunk u at col[u E]
+  int t[25];
+  t[24] = tid < a.E ? a.line[tid] : 0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) t[u] = tid < a.E && u < ch ? col[(int64_t)u * a.E] : 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) t[16 + u] = tid < a.E && u < r ? a.counts[u * a.E + tid] : 0;
+  int sh[kShiftU];
+#pragma unroll
+  for (int u = 0; u < kShiftU; ++u) {
+    const int i = tid + u * kPlanChunk;
+    sh[u] = tab && i < RE ? a.shift[i] : 0;
+  }
+  int ef[kEfixU];
+#pragma unroll
+  for (int u = 0; u < kEfixU; ++u) {
+    const int i = tid + u * kPlanChunk;
+    ef[u] = i < 2 * a.E ? a.efix[i] : 0;
+  }
+  const int pc0 = tab && tid < npc ? a.pieces[tid] : 0;
+  const int np0 = tid < a.R ? a.npieces[tid] : 0;
+  const int err = a.stats[MOONEP_STAT_ERROR];
+  if (!err) {
+    for (int i = tid; i < 4 * a.E; i += kPlanChunk) mask[i / a.E][i % a.E] = 0ull;
+    if (tid < a.E) {
+      int v = 0;
+#pragma unroll
+      for (int u = 0; u < 25; ++u) v += t[u];
+      for (int c0 = 16; c0 < ch; c0 += 16) {            // more than 16 earlier chunks
+#pragma unroll
+        for (int u = 0; u < 16; ++u) t[u] = c0 + u < ch ? col[(int64_t)(c0 + u) * a.E] : 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v += t[u];
+      }
+      for (int q0 = 8; q0 < r; q0 += 8) {                // more than 8 lower ranks
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = q0 + u < r ? a.counts[(q0 + u) * a.E + tid] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v += t[u];
+      }
+      s_base[tid] = v;
+    }
+#pragma unroll
+    for (int u = 0; u < kShiftU; ++u) {
+      const int i = tid + u * kPlanChunk;
+      if (tab && i < RE) s_shift[i] = sh[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kEfixU; ++u) {
+      const int i = tid + u * kPlanChunk;
+      if (i < 2 * a.E) s_efix[i] = ef[u];
+    }
+    if (tab && tid < npc) s_pieces[tid] = pc0;
+    if (tid < a.R) s_np[tid] = np0;
+    // further rounds for larger shapes (each a batch of independent loads)
+    for (int i = tid + kPlanChunk; i < a.E; i += kPlanChunk) {
+      const int32_t* ci = a.cc + (int64_t)r * a.nch * a.E + i;
+      int v = a.line[i];
+      for (int c0 = 0; c0 < ch; c0 += 16) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) t[u] = c0 + u < ch ? ci[(int64_t)(c0 + u) * a.E] : 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v += t[u];
+      }
+      for (int q0 = 0; q0 < r; q0 += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = q0 + u < r ? a.counts[(q0 + u) * a.E + i] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v += t[u];
+      }
       s_base[i] = v;
     }
-    for (int i = tid; i < a.R; i += kPlanChunk) s_np[i] = a.npieces[i];
-    for (int i = tid; i < 2 * a.E; i += kPlanChunk) s_efix[i] = a.efix[i];
     if (tab) {
-      for (int i0 = tid; i0 < a.R * a.E; i0 += 4 * kPlanChunk) {
-        int v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u * kPlanChunk;
-          v[u] = i < a.R * a.E ? a.shift[i] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u * kPlanChunk;
-          if (i < a.R * a.E) s_shift[i] = v[u];
-        }
-      }
-      for (int i = tid; i < npc; i += kPlanChunk) s_pieces[i] = a.pieces[i];
+      for (int i = tid + kShiftU * kPlanChunk; i < RE; i += kPlanChunk) s_shift[i] = a.shift[i];
+      for (int i = tid + kPlanChunk; i < npc; i += kPlanChunk) s_pieces[i] = a.pieces[i];
     }
+    for (int i = tid + kEfixU * kPlanChunk; i < 2 * a.E; i += kPlanChunk) s_efix[i] = a.efix[i];
+    for (int i = tid + kPlanChunk; i < a.R; i += kPlanChunk) s_np[i] = a.npieces[i];
     __syncthreads();
     if (s < a.S)
 #pragma unroll
       for (int k = 0; k < kMaxK; ++k)
         if (k < a.K) atomicOr(&mask[w][ids[k]], bit);
     // the padding range of this thread's row (in flight during the assignment)
-    if (pad_row >= 0) {
-      const int end = a.cu[r * EB + pad_row];
-      const int n = a.segn[r * EB + pad_row];
-      s_plo[tid] = end - round_up(n, a.tp) + n;
-      s_phi[tid] = end;
+    if (pad_n > 0) {
+      s_plo[tid] = pad_end - round_up(pad_n, a.tp) + pad_n;
+      s_phi[tid] = pad_end;
     } else {
       s_plo[tid] = 0;
       s_phi[tid] = 0;
@@ -748,10 +896,9 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
     // rows past the first 256 of the chunk (more than 256 nch active rows), a thread each
     for (int q0 = kPlanChunk; ch + q0 * a.nch < L2; q0 += kPlanChunk) {
       const int q = ch + (q0 + tid) * a.nch;
-      const int row = q < L2 ? a.aux[a.ax.act + r * L2 + q] : -1;
-      if (row >= 0) {
-        const int end = a.cu[r * EB + row];
-        const int n = a.segn[r * EB + row];
+      const int n = q < L2 ? a.an[r * L2 + q] : 0;
+      if (n > 0) {
+        const int end = a.aend[r * L2 + q];
         for (int i = end - round_up(n, a.tp) + n; i < end; ++i) a.src[(int64_t)r * a.NvS + i] = -1;
       }
     }
@@ -784,13 +931,14 @@ hipError_t launch_plan(const Ctx& c, const int32_t* topk, const int32_t* tpe,
   a.topk = topk; a.tpe = tpe;
   a.cc = c.cc; a.chunk_err = c.chunk_err; a.shift = c.shift;
   a.pieces = c.pieces; a.npieces = c.npieces; a.line = c.line; a.efix = c.efix;
+  a.aend = c.aend; a.an = c.an; a.rend = c.rend;
   a.counts = p.counts; a.dest = p.dest; a.src = p.src; a.cu = p.cu_seqlens;
   a.segn = p.seg_tokens; a.pf = p.prefetch_src; a.stats = p.stats; a.aux = p.aux;
   a.ax = d.aux;
   const dim3 grid(d.nch, d.R);
   plan_hist<<<grid, kPlanChunk, 0, s>>>(a);
   plan_solve<<<1, kSolveThreads, 0, s>>>(a);
-  plan_assign<<<dim3(d.nch + 1, d.R), kPlanChunk, 0, s>>>(a);
+  plan_assign<<<dim3(d.nch + 2, d.R), kPlanChunk, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // moonep_plan without a handle and without allocating: the planning scratch
 // (per-chunk expert counts, slot shifts, line pieces, line starts, per-chunk
-// error bits, per-expert destinations) lives in one file-scope device array instead
+// error bits, per-expert destinations, the padded end and token count of each
+// rank's active rows, each rank's used slots) lives in one file-scope device array instead
 // of the handle's device allocations, for callers that cannot allocate device
 // memory (code under HIP graph capture, tight serving loops, harnesses that
 // forbid allocation).  The kernels are the planner's own (launch_plan); only
@@ -33,7 +34,7 @@ int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }   // 256-byte pieces
 // int32 elements of every planning scratch array of `d`, in the order they
 // are carved out of the array.
 struct Carve {
-  int64_t n[7];
+  int64_t n[10];
   int64_t total() const {
     int64_t t = 0;
     for (int64_t v : n) t += pad64(v);
@@ -43,7 +44,8 @@ struct Carve {
 
 Carve carve(const Dims& d) {
   return Carve{{(int64_t)d.R * d.nch * d.E, (int64_t)d.R * d.E, (int64_t)d.R * (d.R + 1) * 2,
-                (int64_t)d.R, (int64_t)d.E, (int64_t)d.R * d.nch, 2LL * d.E}};
+                (int64_t)d.R, (int64_t)d.E, (int64_t)d.R * d.nch, 2LL * d.E, 2LL * d.E,
+                2LL * d.E, (int64_t)d.R}};
 }
 
 bool plan_arrays_ok(const moonep_plan_t* p) {
@@ -93,10 +95,10 @@ extern "C" moonep_status_t moonep_plan_noalloc(const moonep_config_t* cfg, const
   c.d = d;
   c.device = 0;
   c.num_cu_device = 0;
-  int32_t** dst[7] = {&c.cc, &c.shift, &c.pieces, &c.npieces, &c.line, &c.chunk_err,
-                       &c.efix};
+  int32_t** dst[10] = {&c.cc, &c.shift, &c.pieces, &c.npieces, &c.line, &c.chunk_err,
+                        &c.efix, &c.aend, &c.an, &c.rend};
   int64_t off = 0;
-  for (int i = 0; i < 7; ++i) {
+  for (int i = 0; i < 10; ++i) {
     *dst[i] = base + off;
     off += pad64(cv.n[i]);
   }

@@ -54,12 +54,13 @@ struct TileSchedLds {
   int t0[256], tend[256], row[256], end[256], len[256], grp[256];
 };
 
-__device__ __forceinline__ void build_tile_schedule(const int32_t* act, const int32_t* cu,
-                                                    const int32_t* segn, int32_t* tiles,
+// act, aend, an: [R][L2] active rows of each rank, their padded segment ends
+// and real token counts (entries past the rank's last active row: row -1).
+__device__ __forceinline__ void build_tile_schedule(const int32_t* act, const int32_t* aend,
+                                                    const int32_t* an, int32_t* tiles,
                                                     int32_t* ntiles, int32_t* nfull, int d,
-                                                    int L2, int EB,
-                                                    int tp, int max_tiles, int (&wsum)[4],
-                                                    TileSchedLds& sl) {
+                                                    int L2, int tp, int max_tiles,
+                                                    int (&wsum)[4], TileSchedLds& sl) {
   const int tid = threadIdx.x;
   int32_t* rank_tiles = tiles + (int64_t)d * max_tiles * 4;
   auto put = [&](int t, int row, int m0, int m1, int gs, int gm) {
@@ -77,8 +78,8 @@ __device__ __forceinline__ void build_tile_schedule(const int32_t* act, const in
     const int row = q < L2 ? act[d * L2 + q] : -1;
     int end = 0, len = 0, nf = 0;
     if (row >= 0) {
-      end = cu[d * EB + row];
-      len = tile_round_up(segn[d * EB + row], tp);
+      end = aend[d * L2 + q];
+      len = tile_round_up(an[d * L2 + q], tp);
       const int rem = len % kTileM;
       nf = len / kTileM + (rem > kShortTileM ? 1 : 0);
     }
@@ -117,8 +118,8 @@ __device__ __forceinline__ void build_tile_schedule(const int32_t* act, const in
     const int row = q < L2 ? act[d * L2 + q] : -1;
     int end = 0, rem = 0;
     if (row >= 0) {
-      end = cu[d * EB + row];
-      rem = tile_round_up(segn[d * EB + row], tp) % kTileM;
+      end = aend[d * L2 + q];
+      rem = tile_round_up(an[d * L2 + q], tp) % kTileM;
     }
     const int ns = rem > 0 && rem <= kShortTileM ? 1 : 0;
     int total;

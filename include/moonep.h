@@ -149,7 +149,7 @@ moonep_status_t moonep_plan(moonep_handle_t h, const int32_t* topk,
  * MOONEP_NOALLOC_SCRATCH_BYTES in the library's device memory, one per GPU,
  * which the GPU holds until the process ends.  The scratch needed, in int32
  * elements each rounded up to 64, is R*ceil(S/256)*E + R*E + 2*R*(R+1)
- * + R + E + R*ceil(S/256) + 2*E; MOONEP_ERR_SCRATCH (nothing enqueued) when it
+ * + R + E + R*ceil(S/256) + 3*(2*E) + R; MOONEP_ERR_SCRATCH (nothing enqueued) when it
  * exceeds the array (e.g. R=8, E=256 fits up to S of about 64000).  Calls
  * that overlap on one GPU (different streams or host threads) share the
  * array and race; calls on one stream are ordered.  The first call with a
