@@ -552,6 +552,108 @@ def time_per_rank(w, buf, batches, home, pool, x, reps=3):
     return out
 
 
+def _smi_sample():
+    """One amd-smi reading of the GPU: socket power (W) and the shader clock of
+    each XCD (MHz), or None when amd-smi is not available."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "-g", "0"], capture_output=True,
+                           text=True, timeout=30)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    p = re.findall(r"SOCKET_POWER: (\d+) W", r.stdout)
+    c = re.findall(r"GFX_\d+:\s+CLK: (\d+) MHz", r.stdout)
+    if not p or not c:
+        return None
+    return int(p[0]), [int(x) for x in c]
+
+
+def power_probe(w, secs):
+    """Board power and shader clocks while one kind of kernel runs back to
+    back for `secs` seconds (after a warm-up), sampled with amd-smi from a
+    second thread: the idle GPU, a plain 4 GiB copy (HBM traffic alone), and
+    the headline's gate/up GEMM, down GEMM and one weight-gradient GEMM at
+    balanced routing."""
+    import threading
+    import torch
+    from grouped_gemm_moonep_amd import Buffer
+    dev = "cuda"
+    topk, _ = synth.routing(w, 0.0)
+    home = [torch.empty((w.E, w.H, w.Hp), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    for i in range(3):
+        synth.expert_weights_device(w, i, home[i])
+    pool = [torch.zeros((w.R, w.B, w.H, w.Hp), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    buf = Buffer(R=w.R, S=w.S, K=w.K, E=w.E, B=w.B, H=w.H, Hp=w.Hp, token_padding=w.token_padding)
+    plan = buf.plan(torch.from_numpy(topk).to(dev))
+    g = torch.Generator(device=dev).manual_seed(0)
+    x = torch.randn((w.R, w.S, w.H), generator=g, device=dev).to(torch.bfloat16)
+    x_nvs, _ = buf.dispatch(plan, x)
+    z = torch.empty((w.R, buf.NvS, w.Hp), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((w.R, buf.NvS, w.H), dtype=torch.bfloat16, device=dev)
+    a = torch.ones(1 << 30, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    legs = {
+        "idle": None,
+        "copy_4GiB": lambda: b.copy_(a),
+        "ffn_gateup": lambda: buf.expert_gateup(plan, x_nvs, home, pool, z),
+        "ffn_down": lambda: buf.expert_down(plan, z, home, pool, y),
+    }
+    out = {}
+    for name, f in list(legs.items()) + [("wgrad_kernel", "wgrad")]:
+        if f == "wgrad":
+            del legs, a, b
+            home = pool = None
+            torch.cuda.empty_cache()
+            gh = torch.zeros((w.E, w.H, w.Hp), dtype=torch.float32, device=dev)
+            rb = torch.zeros((w.R, w.B, w.H, w.Hp), dtype=torch.float32, device=dev)
+            f = lambda: buf.expert_wgrad(plan, x_nvs, z, gh, rb)
+        print(f"[bench] power: {name}", file=sys.stderr, flush=True)
+        samples, stop = [], threading.Event()
+
+        def sampler():
+            time.sleep(2.0)                       # past the warm-up
+            while not stop.is_set():
+                s = _smi_sample()
+                if s is None:
+                    return
+                samples.append(s)
+                time.sleep(0.25)
+
+        th = threading.Thread(target=sampler)
+        n, t_ms = 0, 0.0
+        if f is not None:
+            f()
+        torch.cuda.synchronize()
+        th.start()
+        t0 = time.time()
+        while time.time() - t0 < secs:
+            if f is None:
+                time.sleep(0.1)
+                continue
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            n += 10
+            t_ms += e0.elapsed_time(e1)
+        stop.set()
+        th.join()
+        if not samples:
+            out[name] = "amd-smi unavailable"
+            continue
+        pw = [p for p, _ in samples]
+        clk = [c for _, cs in samples for c in cs]
+        out[name] = {"samples": len(samples), "socket_power_W": [min(pw), max(pw)],
+                     "shader_clock_MHz_mean": round(float(np.mean(clk)), 1),
+                     "shader_clock_MHz_range": [min(clk), max(clk)],
+                     "launches": n, "ms_per_launch": round(t_ms / n, 3) if n else None}
+    buf.destroy()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -588,6 +690,10 @@ def main():
                     help="per maxvio target: timed repetitions (after 3 warm-up ones) of "
                          "the step, each after a cache flush; the per-target table reports "
                          "their medians")
+    ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
+                    help="only measure board power and shader clocks (amd-smi) while the idle "
+                         "GPU, a 4 GiB copy, gate/up, down and one weight gradient each run "
+                         "for SECONDS at the headline shape, and print them as one JSON line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before warmup, run torch.neg over a float32 buffer of MIB MiB "
                          "three times: a plain kernel of known traffic (reads and writes "
@@ -602,6 +708,11 @@ def main():
     from grouped_gemm_moonep_amd import Buffer
 
     w = synth.WORKLOADS[args.workload]
+    if args.power > 0:
+        print(json.dumps({"power": power_probe(w, args.power), "workload": w.name,
+                          "note": "amd-smi metric -p -c every ~0.3 s from a second thread while "
+                                  "each leg's kernel runs back to back"}), flush=True)
+        return
     dev = "cuda"
     if args.targets is None:
         targets = list(synth.SWEEPS[args.workload])
