@@ -151,6 +151,30 @@ __device__ __forceinline__ void block_scan2(int x, int y, int* ex, int* ey, int*
   *ty = scratch[4 * kSolveWaves - 1];
 }
 
+// Sums of two (rank, expert) columns of the chunk counts (chunk c at col[c E]),
+// KB chunks of each in flight at a time: unconditional loads, the indices
+// clamped into the column and the surplus masked afterwards (a load under a
+// condition becomes a branch with a wait after it).
+template <int KB>
+__device__ __forceinline__ void column_sums(const int32_t* col0, const int32_t* col1, bool has1,
+                                            int nch, int E, int& run0, int& run1) {
+  for (int ch0 = 0; ch0 < nch; ch0 += KB) {
+    int v0[KB], v1[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int c = min(ch0 + u, nch - 1);
+      v0[u] = col0[(int64_t)c * E];
+      v1[u] = col1[(int64_t)c * E];
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const bool ok = ch0 + u < nch;
+      run0 += ok ? v0[u] : 0;
+      run1 += ok && has1 ? v1[u] : 0;
+    }
+  }
+}
+
 // Wave-wide sum (all 64 lanes get it).
 __device__ __forceinline__ int wave_sum(int v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -189,29 +213,17 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   // error bits loaded beside them.  (Each plan_assign workgroup sums the
   // chunks before its own, so nothing is written back here.)
   {
-    constexpr int kBatch = 8;            // chunk loads per column in flight
-    int cerr = 0;
-    for (int i = tid; i < R * nch; i += kSolveThreads) cerr |= a.chunk_err[i];
+    // the first 1024 chunks' error bits load beside the counts (a loop of its
+    // own would wait for them first)
+    int cerr = a.chunk_err[min(tid, R * nch - 1)];
+    for (int i = tid + kSolveThreads; i < R * nch; i += kSolveThreads) cerr |= a.chunk_err[i];
     for (int i0 = tid; i0 < RE; i0 += 2 * kSolveThreads) {
       const int i1 = i0 + kSolveThreads;
       const bool has1 = i1 < RE;
       const int32_t* col0 = a.cc + (int64_t)(i0 / E) * nch * E + (i0 % E);
       const int32_t* col1 = has1 ? a.cc + (int64_t)(i1 / E) * nch * E + (i1 % E) : col0;
       int run0 = 0, run1 = 0;
-      for (int ch0 = 0; ch0 < nch; ch0 += kBatch) {
-        int v0[kBatch], v1[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const bool ok = ch0 + u < nch;
-          v0[u] = ok ? col0[(int64_t)(ch0 + u) * E] : 0;
-          v1[u] = ok && has1 ? col1[(int64_t)(ch0 + u) * E] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          run0 += v0[u];
-          run1 += v1[u];
-        }
-      }
+      column_sums<16>(col0, col1, has1, nch, E, run0, run1);
       a.counts[i0] = run0;
       atomicAdd(&T[i0 % E], run0);
       if (a.tpe && a.tpe[i0] != run0) cerr |= MOONEP_ROUTE_COUNTS;
@@ -263,11 +275,19 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
         const int g = e / L;
         te = T[e];
         const int f0 = g * L + (part * L) / 4, f1 = g * L + ((part + 1) * L) / 4;
-#pragma unroll 4
-        for (int f = f0; f < f1; ++f) {
-          const int tf = T[f];
-          acc += (tf < te || (tf == te && f < e)) ? tf : 0;
-          tot += tf;
+        // eight loads in flight, then their sums (read one by one, each LDS
+        // read's latency was exposed)
+        for (int b = f0; b < f1; b += 8) {
+          int tf[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) tf[u] = T[min(b + u, E - 1)];   // masked below
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int f = b + u;
+            const int v = f < f1 ? tf[u] : 0;
+            acc += (v < te || (v == te && f < e)) ? v : 0;
+            tot += v;
+          }
         }
       }
       acc += __shfl_xor(acc, 1, 64);
@@ -301,11 +321,17 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     recv_lo[g] = 0;
     recv_hi[g] = 0;
     int pd = 0, pr = 0;
-    for (int h = 0; h < R; ++h) {
-      const int wh = W[h];
-      const int xh = wh > C ? wh - C : 0, dh = wh < C ? C - wh : 0;
-      pd += xh > 0 && (xh > xg || (xh == xg && h < g));
-      pr += dh > 0 && (dh > dg || (dh == dg && h < g));
+    for (int h0 = 0; h0 < R; h0 += 8) {             // eight loads in flight
+      int wv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) wv[u] = W[min(h0 + u, R - 1)];     // masked below
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int h = h0 + u, wh = h < R ? wv[u] : C;   // past R: neither donor nor receiver
+        const int xh = wh > C ? wh - C : 0, dh = wh < C ? C - wh : 0;
+        pd += xh > 0 && (xh > xg || (xh == xg && h < g));
+        pr += dh > 0 && (dh > dg || (dh == dg && h < g));
+      }
     }
     if (xg > 0) {
       donors[pd] = g;
@@ -440,8 +466,13 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
         row = d * L + i;
       } else {
         int j = 0;
-#pragma unroll 8
-        for (int q = L; q < i; ++q) j += ent_n[d * L2 + q] > 0;
+        for (int q0 = L; q0 < i; q0 += 8) {          // eight loads in flight
+          int nv[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) nv[u] = ent_n[d * L2 + min(q0 + u, L2 - 1)];   // masked below
+#pragma unroll
+          for (int u = 0; u < 8; ++u) j += q0 + u < i && nv[u] > 0;
+        }
         row = j < B ? E + j : recv_g[d] * L + (i - L);
       }
     }
@@ -736,13 +767,28 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
   const int RE = a.R * a.E;
   constexpr int kShiftU = 12;                      // shift entries per thread in the first round
   constexpr int kEfixU = 4;                        // shortcut entries per thread in the first round
-  const int32_t* col = a.cc + (int64_t)r * a.nch * a.E + tid;      // chunk u at col[u E]
-  int t[25];
-  t[24] = tid < a.E ? a.line[tid] : 0;
+  // experts tid and tid + 256 (the second only when E > 256); indices are
+  // clamped into range and the surplus masked when summing, so no load sits
+  // under a lane condition
+  const int32_t* colr = a.cc + (int64_t)r * a.nch * a.E;   // chunk c of expert e at colr[c E + e]
+  const int cmax = ch > 0 ? ch - 1 : 0, rmax = r > 0 ? r - 1 : 0;
+  const bool two = a.E > kPlanChunk;
+  const int ex0 = min(tid, a.E - 1), ex1 = min(tid + kPlanChunk, a.E - 1);
+  int t[25], t1[25];
+  t[24] = a.line[ex0];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) t[u] = tid < a.E && u < ch ? col[(int64_t)u * a.E] : 0;
+  for (int u = 0; u < 16; ++u) t[u] = colr[(int64_t)min(u, cmax) * a.E + ex0];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) t[16 + u] = tid < a.E && u < r ? a.counts[u * a.E + tid] : 0;
+  for (int u = 0; u < 8; ++u) t[16 + u] = a.counts[min(u, rmax) * a.E + ex0];
+#pragma unroll
+  for (int u = 0; u < 25; ++u) t1[u] = 0;
+  if (two) {
+    t1[24] = a.line[ex1];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) t1[u] = colr[(int64_t)min(u, cmax) * a.E + ex1];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t1[16 + u] = a.counts[min(u, rmax) * a.E + ex1];
+  }
   int sh[kShiftU];
 #pragma unroll
   for (int u = 0; u < kShiftU; ++u) {
@@ -760,23 +806,48 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
   const int err = a.stats[MOONEP_STAT_ERROR];
   if (!err) {
     for (int i = tid; i < 4 * a.E; i += kPlanChunk) mask[i / a.E][i % a.E] = 0ull;
-    if (tid < a.E) {
-      int v = 0;
+    {
+      // the line start, the first 16 earlier chunks and 8 lower ranks of both experts
+      int v0 = t[24], v1 = t1[24];
 #pragma unroll
-      for (int u = 0; u < 25; ++u) v += t[u];
-      for (int c0 = 16; c0 < ch; c0 += 16) {            // more than 16 earlier chunks
-#pragma unroll
-        for (int u = 0; u < 16; ++u) t[u] = c0 + u < ch ? col[(int64_t)(c0 + u) * a.E] : 0;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) v += t[u];
+      for (int u = 0; u < 16; ++u) {
+        v0 += u < ch ? t[u] : 0;
+        v1 += u < ch ? t1[u] : 0;
       }
-      for (int q0 = 8; q0 < r; q0 += 8) {                // more than 8 lower ranks
 #pragma unroll
-        for (int u = 0; u < 8; ++u) t[u] = q0 + u < r ? a.counts[(q0 + u) * a.E + tid] : 0;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v += t[u];
+      for (int u = 0; u < 8; ++u) {
+        v0 += u < r ? t[16 + u] : 0;
+        v1 += u < r ? t1[16 + u] : 0;
       }
-      s_base[tid] = v;
+      // further rounds (both experts' loads together) past 16 chunks or 8 ranks
+      for (int c0 = 16; c0 < ch; c0 += 16) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int c = min(c0 + u, cmax);
+          t[u] = colr[(int64_t)c * a.E + ex0];
+          t1[u] = two ? colr[(int64_t)c * a.E + ex1] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          v0 += c0 + u < ch ? t[u] : 0;
+          v1 += c0 + u < ch ? t1[u] : 0;
+        }
+      }
+      for (int q0 = 8; q0 < r; q0 += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int q = min(q0 + u, rmax);
+          t[u] = a.counts[q * a.E + ex0];
+          t1[u] = two ? a.counts[q * a.E + ex1] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          v0 += q0 + u < r ? t[u] : 0;
+          v1 += q0 + u < r ? t1[u] : 0;
+        }
+      }
+      if (tid < a.E) s_base[tid] = v0;
+      if (two && tid + kPlanChunk < a.E) s_base[tid + kPlanChunk] = v1;
     }
 #pragma unroll
     for (int u = 0; u < kShiftU; ++u) {
@@ -791,7 +862,7 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
     if (tab && tid < npc) s_pieces[tid] = pc0;
     if (tid < a.R) s_np[tid] = np0;
     // further rounds for larger shapes (each a batch of independent loads)
-    for (int i = tid + kPlanChunk; i < a.E; i += kPlanChunk) {
+    for (int i = tid + 2 * kPlanChunk; i < a.E; i += kPlanChunk) {
       const int32_t* ci = a.cc + (int64_t)r * a.nch * a.E + i;
       int v = a.line[i];
       for (int c0 = 0; c0 < ch; c0 += 16) {
@@ -838,8 +909,13 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
       for (int k = 0; k < kMaxK; ++k) {
         if (k >= a.K) break;
         const int e = ids[k];
-        int below = __popcll(mask[w][e] & (bit - 1));
-        for (int v = 0; v < w; ++v) below += __popcll(mask[v][e]);
+        // the token's rank among the chunk's tokens of expert e: earlier lanes of
+        // its wave and all lanes of the waves before (the four masks read together)
+        const unsigned long long m0 = mask[0][e], m1 = mask[1][e], m2 = mask[2][e],
+                                 m3 = mask[3][e];
+        const unsigned long long mw = w == 0 ? m0 : w == 1 ? m1 : w == 2 ? m2 : m3;
+        const int below = __popcll(mw & (bit - 1)) + (w > 0 ? __popcll(m0) : 0) +
+                          (w > 1 ? __popcll(m1) : 0) + (w > 2 ? __popcll(m2) : 0);
         const int pos = s_base[e] + below;
         int d = s_efix[2 * e];
         int slot;
@@ -851,15 +927,16 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
           const int32_t* pg = (tab ? (const int32_t*)s_pieces : a.pieces) + (int64_t)g * (a.R + 1) * 2;
           const int np = s_np[g];
           // the first piece whose end lies past pos: count the pieces ending at or
-          // before it (ends ascend), eight independent reads at a time
+          // before it (ends ascend), eight independent reads at a time (indices
+          // clamped to the group's pieces, the surplus masked)
           int cnt = 0;
+          const int plast = np > 0 ? np - 1 : 0;
           for (int p0 = 0; p0 < np; p0 += 8) {
+            int hv[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const int p = p0 + u;
-              const int hi = p < np ? pg[2 * p] : 0x7FFFFFFF;
-              cnt += pos >= hi ? 1 : 0;
-            }
+            for (int u = 0; u < 8; ++u) hv[u] = pg[2 * min(p0 + u, plast)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) cnt += p0 + u < np && pos >= hv[u] ? 1 : 0;
           }
           d = cnt < np ? pg[2 * cnt + 1] : pg[1];
           slot = (unsigned)d < (unsigned)a.R
