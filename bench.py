@@ -837,6 +837,17 @@ def main():
         sw[t] = {n: [ev[j].elapsed_time(ev[j + 1]) * 1e-3 for ev in evs]
                  for j, n in enumerate(names)}
         sw[t]["ffn"] = [a + b for a, b in zip(sw[t]["gateup"], sw[t]["down"])]
+        # the plan alone, back to back after one cache flush (in the step it follows
+        # the previous step's FFN, whose power state slows this latency-bound kernel chain)
+        flush()
+        pe = [torch.cuda.Event(enable_timing=True) for _ in range(args.sweep_reps + 4)]
+        _, topk_t, _ = batches[ti]
+        pe[0].record()
+        for r in range(args.sweep_reps + 3):
+            buf.plan(topk_t, plan=plan)
+            pe[r + 1].record()
+        torch.cuda.synchronize()
+        sw[t]["plan_b2b"] = [pe[r].elapsed_time(pe[r + 1]) * 1e-3 for r in range(3, args.sweep_reps + 3)]
 
     sweep = {}
     for t in targets:
@@ -846,7 +857,9 @@ def main():
         sweep[str(t)] = {
             "realized_maxvio": round(stats[t]["maxvio"], 4), "dups": stats[t]["dups"],
             "pad_rows": stats[t]["pad_rows"],
-            "plan_us": round(m("plan") * 1e6, 2), "dispatch_us": round(m("dispatch") * 1e6, 1),
+            "plan_us": round(m("plan") * 1e6, 2),
+            "plan_back_to_back_us": round(m("plan_b2b") * 1e6, 2),
+            "dispatch_us": round(m("dispatch") * 1e6, 1),
             "prefetch_us": round(m("prefetch") * 1e6, 1), "ffn_ms": round(m("ffn") * 1e3, 3),
             "gateup_ms": round(m("gateup") * 1e3, 3), "down_ms": round(m("down") * 1e3, 3),
             "combine_us": round(m("combine") * 1e6, 1),
@@ -949,7 +962,9 @@ def main():
                         f"written before every timed step (outside the stage events, inside "
                         f"ms_per_step) so the last-level cache holds none of the step's inputs; "
                         f"value and roofline: mean over the {args.steps} timed steps; sweep: "
-                        f"medians of {args.sweep_reps} steps per target")
+                        f"medians of {args.sweep_reps} steps per target (plan_back_to_back_us: "
+                        f"medians of {args.sweep_reps} plans in a row after one flush, outside "
+                        f"the steps)")
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         t1 = 1.0 if 1.0 in host_routing else targets[0]
