@@ -205,6 +205,18 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     s_err = 0; s_maxload = 0; s_ndon = 0; s_dups = 0; s_pad = 0; s_nd = 0; s_nq = 0;
   }
   for (int e = tid; e < E; e += kSolveThreads) T[e] = 0;
+  // phase F's visit-order slots and per-rank counts (cleared here, where a
+  // barrier follows anyway)
+  const int S3 = 3 * L;
+  const int nslot = R * S3;
+  for (int i = tid; i < nslot; i += kSolveThreads) {
+    ord_len[i] = 0;
+    ord_ent[i] = -1;
+  }
+  for (int d = tid; d < R; d += kSolveThreads) {
+    nrem[d] = 0;
+    npf[d] = 0;
+  }
   __syncthreads();
 
   // Phase A: counts per (r, e) summed over the chunks and the expert loads
@@ -456,12 +468,20 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     ent_lo[idx] = rlo;
   }
   __syncthreads();
-  // rows: home experts use their own row; the j-th remote expert with tokens
-  // (ascending id) prefetch row E+j while j < B, its home row after that
+  // Rows: home experts use their own row; the j-th remote expert with tokens
+  // (ascending id) prefetch row E+j while j < B, its home row after that.
+  // Phase F starts in the same loop: each rank's active rows are laid out in
+  // ascending row order, the lower group's rows first (the rank's home
+  // experts or the remote experts that keep home rows), prefetch rows last;
+  // every active entry takes a visit-order slot (3L per rank), and one
+  // block-wide scan over all slots (below) gives each row's start and its
+  // index among the rank's active rows.  Per rank: its remote experts and
+  // used prefetch rows.
   for (int idx = tid; idx < R * L2; idx += kSolveThreads) {
     const int d = idx / L2, i = idx - (idx / L2) * L2;
+    const int n = ent_n[idx];
     int row = -1;
-    if (ent_n[idx] > 0) {
+    if (n > 0) {
       if (i < L) {
         row = d * L + i;
       } else {
@@ -475,61 +495,22 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
         }
         row = j < B ? E + j : recv_g[d] * L + (i - L);
       }
+      const int g = recv_g[d];
+      const bool home_first = g < 0 || d < g;
+      const bool pf = row >= E;
+      int o;
+      if (i < L) o = (home_first ? 0 : L) + i;
+      else if (pf) o = 2 * L + (i - L);
+      else o = (home_first ? L : 0) + (i - L);
+      ord_len[d * S3 + o] = round_up(n, a.tp);
+      ord_ent[d * S3 + o] = idx;
+      if (i >= L) atomicAdd(&nrem[d], 1);    // the rank's remote experts
+      if (pf) atomicAdd(&npf[d], 1);         // of which in prefetch rows
     }
     ent_row[idx] = row;
   }
   __syncthreads();
 
-  // Phase F: lay each rank's active rows out in ascending row order: the
-  // lower group's rows first (the rank's home experts or the remote experts
-  // that keep home rows), prefetch rows last.  Every active entry gets a
-  // visit-order slot (3L per rank); one block-wide scan over all slots gives
-  // each row's start and its index among the rank's active rows.  Per rank:
-  // its remote experts and used prefetch rows, counted by one thread.
-  const int S3 = 3 * L;
-  const int nslot = R * S3;
-  for (int i = tid; i < nslot; i += kSolveThreads) {
-    ord_len[i] = 0;
-    ord_ent[i] = -1;
-  }
-  for (int d = tid; d < R; d += kSolveThreads) {
-    nrem[d] = 0;
-    npf[d] = 0;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < R * L2; idx += kSolveThreads) {
-    const int n = ent_n[idx];
-    if (n == 0) continue;
-    const int d = idx / L2, i = idx - (idx / L2) * L2;
-    const int g = recv_g[d];
-    const bool home_first = g < 0 || d < g;
-    const bool pf = ent_row[idx] >= E;
-    int o;
-    if (i < L) o = (home_first ? 0 : L) + i;
-    else if (pf) o = 2 * L + (i - L);
-    else o = (home_first ? L : 0) + (i - L);
-    ord_len[d * S3 + o] = round_up(n, a.tp);
-    ord_ent[d * S3 + o] = idx;
-    if (i >= L) atomicAdd(&nrem[d], 1);      // the rank's remote experts
-    if (pf) atomicAdd(&npf[d], 1);           // of which in prefetch rows
-  }
-  __syncthreads();
-  // prefix of the used prefetch rows over the ranks (one wave)
-  if (tid < 64) {
-    int run = 0;
-    for (int d0 = 0; d0 < R; d0 += 64) {
-      const int d = d0 + tid;
-      const int v = d < R ? npf[d] : 0;
-      int x = v;
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (tid >= o) x += y;
-      }
-      if (d < R) pfpre[d] = run + x - v;
-      run += __shfl(x, 63, 64);
-    }
-  }
-  __syncthreads();
   int tot_cnt, tot_len;
   {
     const int per = (nslot + kSolveThreads - 1) / kSolveThreads;
@@ -576,6 +557,16 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   }
   __syncthreads();
   for (int d = tid; d < R; d += kSolveThreads) {
+    // the used prefetch rows of the ranks before d (eight loads in flight)
+    int pre = 0;
+    for (int h0 = 0; h0 < d; h0 += 8) {
+      int nv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) nv[u] = npf[min(h0 + u, R - 1)];   // masked below
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pre += h0 + u < d ? nv[u] : 0;
+    }
+    pfpre[d] = pre;
     const int next = d + 1 < R ? ord_cnt[(d + 1) * S3] : tot_cnt;
     nact[d] = next - ord_cnt[d * S3];
     a.aux[a.ax.nact + d] = nact[d];
