@@ -555,7 +555,8 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
     pad = wave_sum(pad);
     if ((tid & 63) == 0 && pad) atomicAdd(&s_pad, pad);
   }
-  __syncthreads();
+  // per rank, in the same pass (it reads only the scan's prefixes and the
+  // counts of the rows loop)
   for (int d = tid; d < R; d += kSolveThreads) {
     // the used prefetch rows of the ranks before d (eight loads in flight)
     int pre = 0;
