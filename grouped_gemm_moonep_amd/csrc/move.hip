@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyArgs a) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int v = v0 + u * 64 + lane;
-        if (v < a.nv) t[v] = buf[u];
+        if (v < a.nv) __builtin_nontemporal_store(buf[u], t + v);   // 2-3% faster than plain
       }
     }
   }
