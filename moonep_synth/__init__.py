@@ -141,6 +141,31 @@ def routing_adversarial(w: Workload, seed: int = 0):
     return topk, _softmax_f32(logits)
 
 
+def _topk_of(scores: np.ndarray, K: int):
+    order = np.argsort(-scores, axis=-1, kind="stable")[..., :K]
+    chosen = np.take_along_axis(scores, order, axis=-1)
+    return order.astype(np.int32), _softmax_f32(chosen)
+
+
+def routing_rank_skew(w: Workload, strength: float, seed: int = 0):
+    """Every rank prefers the experts homed on the next rank: logits ~ N(0,1)
+    plus `strength` on experts of group (r+1) mod R for the tokens of rank r
+    (the home groups' loads stay equal while every rank sends its traffic away)."""
+    logits = rng(seed, STREAM_LOGITS).standard_normal((w.R, w.S, w.E), dtype=np.float32)
+    L = w.E // w.R
+    for r in range(w.R):
+        g = (r + 1) % w.R
+        logits[r, :, g * L:(g + 1) * L] += np.float32(strength)
+    return _topk_of(logits, w.K)
+
+
+def routing_hot(w: Workload, nhot: int, seed: int = 0):
+    """Experts 0..nhot-1 (nhot <= K) in every token, the rest of its K at random."""
+    logits = rng(seed, STREAM_LOGITS).standard_normal((w.R, w.S, w.E), dtype=np.float32)
+    logits[..., :nhot] += np.float32(100.0)
+    return _topk_of(logits, w.K)
+
+
 def zipf_scale(name: str, target) -> float:
     with open(ZIPF_TABLE) as f:
         table = json.load(f)
