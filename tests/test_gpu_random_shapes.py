@@ -1,7 +1,9 @@
 """Seeded random shapes through the whole path against the oracle: ranks 1-8,
 1-4 home experts per rank, K up to 8, 0 to E/R prefetch slots, token
-padding 1-128, hidden and FFN widths any multiple of 64 up to 1024, Zipf
-routing strength 0-3.  Each case checks dispatch (bit-exact on every used
+padding 1-128, hidden and FFN widths any multiple of 64 up to 1024; Zipf
+routing strength 0-3 in the first 24 cases, then rank-skewed routing (every
+rank sends to the next rank's experts), hot experts in every token and all
+tokens on the first K experts.  Each case checks dispatch (bit-exact on every used
 slot), the grouped FFN (rel-L2 <= 1e-2 and max(2e-2, 1 ulp)), combine of the
 oracle's FFN output (bit-exact) and, where B = E/R, the FFN backward (2 ulps
 for dG, dU, dX).  The shapes mix segment lengths that leave every kind of
@@ -32,12 +34,24 @@ def _shape(case):
     return synth.Workload(f"rand{case}", R=R, S=S, K=K, E=E, B=B, H=H, Hp=Hp, token_padding=tp), s
 
 
-@pytest.mark.parametrize("case", range(24))
+def _routing(w, s, case):
+    if case < 24:
+        return synth.routing_zipf(w, s, seed=case), f"zipf s={s}"
+    kind = case % 3
+    if kind == 0:
+        return synth.routing_rank_skew(w, 1.0 + s, seed=case), f"rank-skew {1.0 + s}"
+    if kind == 1:
+        nhot = 1 + case % w.K
+        return synth.routing_hot(w, nhot, seed=case), f"hot {nhot}"
+    return synth.routing_adversarial(w, seed=case), "adversarial"
+
+
+@pytest.mark.parametrize("case", range(36))
 def test_random_shape_path(case):
     w, s = _shape(case)
     R, B, H, Hp = w.R, w.B, w.H, w.Hp
-    log(f"random shape {case}: {w} s={s}")
-    topk, rw = synth.routing_zipf(w, s, seed=case)
+    (topk, rw), desc = _routing(w, s, case)
+    log(f"random shape {case}: {w} {desc}")
     p = oracle.plan(topk, w.E, B, w.token_padding)
     x = synth.hidden(w)
     x_nvs, rw_nvs = oracle.dispatch(p, x, rw)
