@@ -87,6 +87,15 @@ def test_plan_edge_shapes(w, s):
     run_and_compare(w, topk)
 
 
+def test_plan_long_sequence():
+    """S = 32768 tokens per rank: 128 planning chunks per rank, so the chunk
+    sums and the assignment's chunk bases take several rounds of loads."""
+    w = synth.Workload("long_r8_s32768_k8_e256", R=8, S=32768, K=8, E=256, B=32, H=64, Hp=64,
+                       token_padding=128)
+    topk, _ = synth.routing_zipf(w, 0.4, seed=3)
+    run_and_compare(w, topk, full_check=False)
+
+
 def test_plan_adversarial_small():
     w = dataclasses.replace(synth.WORKLOADS["mid_r8_s1024_k4_e32"], name="adv")
     topk, _ = synth.routing_adversarial(w)
