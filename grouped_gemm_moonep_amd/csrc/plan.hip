@@ -188,7 +188,6 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(PlanArgs a) {
   __shared__ int aline[kMaxE];
   __shared__ int W[kMaxR], keep[kMaxR], X[kMaxR], need[kMaxR];
   __shared__ int donors[kMaxR], queue[2 * kMaxR + 2];
-  __shared__ int don_g[kMaxR + 1], don_r[kMaxR + 1], don_amt[kMaxR + 1];
   __shared__ int recv_g[kMaxR], recv_lo[kMaxR], recv_hi[kMaxR];
   __shared__ int ent_n[2 * kMaxE], ent_lo[2 * kMaxE], ent_row[2 * kMaxE];
   __shared__ int act_row[2 * kMaxE];
