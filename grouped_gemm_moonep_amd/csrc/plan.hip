@@ -612,7 +612,7 @@ constexpr int kPiecesLds = 1024;    // piece table staged in LDS up to this many
 __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
   const int tid = threadIdx.x;
   const int L2 = 2 * a.L, EB = a.E + a.B;
-  if (blockIdx.x == a.nch) {
+  if ((int)blockIdx.x == a.nch) {
     // the grid's first extra column: rank d's cu_seqlens and seg_tokens, then its
     // grouped-GEMM tile schedule, both from plan_solve's active rows, alongside the
     // token assignment
@@ -646,7 +646,7 @@ __global__ __launch_bounds__(kPlanChunk) void plan_assign(PlanArgs a) {
                         wsum, sl);
     return;
   }
-  if (blockIdx.x == a.nch + 1) {
+  if ((int)blockIdx.x == a.nch + 1) {
     // the second extra column (one workgroup): the reduce_grad tables.  The home
     // experts that have prefetch copies (ascending), the first holder of each and
     // their count, and the holder slots d B + j of each expert in ascending rank.

@@ -38,7 +38,7 @@ struct Mapping {
 struct Chunks {
   std::vector<hipMemGenericAllocationHandle_t> h;
   ~Chunks() {
-    for (auto x : h) hipMemRelease(x);
+    for (auto x : h) (void)hipMemRelease(x);   // best effort at teardown
   }
 };
 
@@ -185,7 +185,7 @@ moonep_status_t moonep_symbuf_create(moonep_handle_t h, int32_t elem_bytes,
   for (size_t i = 0; i < b->ranges.size() && e == hipSuccess; ++i)
     e = hipMemSetAccess(b->ranges[i].va, b->ranges[i].size, &acc, 1);
   if (e != hipSuccess) {
-    release(b);
+    (void)release(b);   // the first error is the one reported
     delete b;
     return st != MOONEP_OK ? st : MOONEP_ERR_HIP;
   }
@@ -212,7 +212,7 @@ moonep_status_t moonep_symbuf_destroy(moonep_symbuf_t b) {
   hipError_t e = hipGetDevice(&cur);
   if (e == hipSuccess && cur != b->device) e = hipSetDevice(b->device);
   if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (cur != b->device) hipSetDevice(cur);
+  if (cur != b->device) (void)hipSetDevice(cur);   // restore the caller's device
   hipError_t r = release(b);
   delete b;
   return (e == hipSuccess && r == hipSuccess) ? MOONEP_OK : MOONEP_ERR_HIP;
