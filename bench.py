@@ -245,6 +245,7 @@ def time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool, steps, warmup,
     names = ["combine_bwd", "ffn_bwd", "dispatch_bwd", "wgrad_x3", "reduce_grad"]
     per = {n: [] for n in names}
     wgrad_bytes = []
+    reduce_bytes = []
     used = []
     EB = w.E + w.B
     for i in range(warmup + steps):
@@ -280,6 +281,12 @@ def time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool, steps, warmup,
             rows = int(plan.arrays["cu_seqlens"].cpu().numpy().reshape(w.R, EB)[:, -1].sum())
             wgrad_bytes.append(3 * int((seg > 0).sum()) * float(w.H) * w.Hp * 4 * 2
                                + 3 * rows * (w.H + w.Hp) * 2)
+            # reduce_grad, per projection: each home row with copies read and written
+            # once, each holder slot read once and zeroed (fp32 rows of H H')
+            ps = plan.arrays["prefetch_src"].cpu().numpy()
+            holders = int((ps >= 0).sum())
+            homes = len(set(int(e) for e in ps[ps >= 0]))
+            reduce_bytes.append(3 * float(w.H) * w.Hp * 4 * (2 * homes + 2 * holders))
     slots = w.R * w.S * w.K
     hh = float(w.H) * w.Hp
     mean = {n: float(np.mean(v)) for n, v in per.items()}
@@ -301,6 +308,16 @@ def time_backward(w, buf, plan, batches, x_nvs, z_ws, home, pool, steps, warmup,
         "frac": round(max(t_mfma, t_hbm) / mean["wgrad_x3"], 4),
         "frac_of_bf16_peak": round(t_mfma / mean["wgrad_x3"], 4),
         "algorithmic_bytes": wb, "flops": 6 * hh * slots}
+    # reduce_grad over the steps that have prefetch copies (balanced routing has none)
+    rt = [t for t, b in zip(per["reduce_grad"], reduce_bytes) if b > 0]
+    if rt:
+        rgbs = sum(b for b in reduce_bytes if b > 0) / sum(rt) / 1e9
+        out["reduce_grad_GBps"] = round(rgbs, 1)
+        out["roofline_reduce_grad"] = {
+            "kernel": "reduce_grad_kernel (three projections, all ranks)", "bound": "hbm",
+            "achieved": round(rgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(rgbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_mean": float(np.mean([b for b in reduce_bytes if b > 0]))}
     pb, db, cb = alg_bytes(w)
     out["combine_bwd_GBps"] = round(db / mean["combine_bwd"] / 1e9, 1)
     out["dispatch_bwd_GBps"] = round((slots * 2 * w.H + w.R * w.S * 2 * w.H + 4 * slots)
