@@ -64,6 +64,7 @@ def lib():
         "moonep_status_string": (ctypes.c_char_p, [i32]),
         "moonep_nvs": (i64, [ctypes.POINTER(MoonepConfig)]),
         "moonep_plan_len": (i64, [ctypes.POINTER(MoonepConfig), i32]),
+        "moonep_launch_grid": (i64, [ctypes.POINTER(MoonepConfig), i32, i32, i32]),
         "moonep_create": (i32, [ctypes.POINTER(MoonepConfig), ctypes.POINTER(vp)]),
         "moonep_destroy": (i32, [vp]),
         "moonep_plan": (i32, [vp, vp, vp, ctypes.POINTER(MoonepPlan), vp]),
@@ -120,6 +121,14 @@ def nvs(cfg: MoonepConfig) -> int:
 
 def plan_len(cfg: MoonepConfig, which: int) -> int:
     return int(lib().moonep_plan_len(ctypes.byref(cfg), which))
+
+
+GRID_DISPATCH, GRID_COMBINE, GRID_COPY, GRID_PREFETCH, GRID_REDUCE_GRAD = range(5)
+
+
+def launch_grid(cfg: MoonepConfig, which: int, W: int = 0, device_cus: int = 256) -> int:
+    """Workgroups a data-movement call would launch (host only)."""
+    return int(lib().moonep_launch_grid(ctypes.byref(cfg), which, W, device_cus))
 
 
 def ptr3(ts):

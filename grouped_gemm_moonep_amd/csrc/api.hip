@@ -171,6 +171,24 @@ int64_t moonep_plan_len(const moonep_config_t* cfg, int32_t which) {
   }
 }
 
+int64_t moonep_launch_grid(const moonep_config_t* cfg, int32_t which, int32_t W,
+                           int32_t device_cus) {
+  Ctx c;
+  if (!dims_from_config(cfg, &c.d) || device_cus < 1) return -1;
+  c.num_cu_device = device_cus;
+  const bool rows = which == MOONEP_GRID_DISPATCH || which == MOONEP_GRID_COMBINE ||
+                    which == MOONEP_GRID_COPY;
+  if (rows && (W <= 0 || W % 8)) return -1;
+  switch (which) {
+    case MOONEP_GRID_DISPATCH: return dispatch_grid(c, W).blocks;
+    case MOONEP_GRID_COMBINE: return combine_grid(c, W);
+    case MOONEP_GRID_COPY: return copy_grid(c);
+    case MOONEP_GRID_PREFETCH: return prefetch_grid(c);
+    case MOONEP_GRID_REDUCE_GRAD: return reduce_grad_grid(c);
+    default: return -1;
+  }
+}
+
 moonep_status_t moonep_create(const moonep_config_t* cfg, moonep_handle_t* out) {
   if (!out) return MOONEP_ERR_ARG;
   Dims d;

@@ -76,6 +76,21 @@ struct WeightRef {
 // Kernel launchers (each returns hipGetLastError() after its launches).
 hipError_t launch_plan(const Ctx& c, const int32_t* topk, const int32_t* tpe,
                        const moonep_plan_t& p, hipStream_t s);
+// Workgroups of each data-movement launch (move.hip); dispatch also needs the
+// split of its grid into token and padding workgroups.
+struct DispatchGrid {
+  int xcd_local;      // 1: one item per wave, a token's waves on one XCD; 0: a capped grid
+  int item_blocks;    // token workgroups (the padding workgroups follow them)
+  int npad_used;      // padding items: (rank, active row, part)
+  int pad_parts;      // parts each active row's padding is split into
+  int64_t blocks;     // the whole grid
+};
+DispatchGrid dispatch_grid(const Ctx& c, int W);
+int64_t combine_grid(const Ctx& c, int W);
+int64_t copy_grid(const Ctx& c);
+int64_t prefetch_grid(const Ctx& c);
+int64_t reduce_grad_grid(const Ctx& c);
+
 hipError_t launch_dispatch(const Ctx& c, const moonep_plan_t& p,
                            const uint16_t* x, int W, const float* rw,
                            uint16_t* x_nvs, float* rw_nvs, hipStream_t s);

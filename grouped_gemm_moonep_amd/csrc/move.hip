@@ -345,6 +345,18 @@ __global__ __launch_bounds__(kThreads) void copy_rows_kernel(CopyArgs a) {
   }
 }
 
+int prefetch_chunks(const Dims& d) {
+  const int64_t row_vecs = (int64_t)d.H * d.Hp / 8;
+  return (int)((row_vecs + kThreads * kPrefetchVecs - 1) / (kThreads * kPrefetchVecs));
+}
+
+constexpr int kReduceChunkVecs = kThreads * 16;   // 64 KiB of fp32 per reduce_grad work item
+
+int reduce_chunks(const Dims& d) {
+  const int64_t row_vecs = (int64_t)d.H * d.Hp / 4;
+  return (int)((row_vecs + kReduceChunkVecs - 1) / kReduceChunkVecs);
+}
+
 int capped_grid(const Ctx& c, int64_t want) {
   int64_t cap = want;
   if (c.d.num_cus > 0) cap = (int64_t)c.d.num_cus * 8;
@@ -353,6 +365,53 @@ int capped_grid(const Ctx& c, int64_t want) {
 }
 
 }  // namespace
+
+// Grid sizes of the data-movement launches (workgroups), shared by the
+// launchers below and by moonep_launch_grid.  With a CU budget (num_cus > 0)
+// every grid is at most num_cus * 8.
+DispatchGrid dispatch_grid(const Ctx& c, int W) {
+  const Dims& d = c.d;
+  DispatchGrid g;
+  const int nv = W / 8;
+  g.pad_parts = (d.tp + 4 * kWaves - 1) / (4 * kWaves);
+  g.npad_used = d.R * 2 * d.L * g.pad_parts;
+  const int nch = (nv + 64 * kDispVecs - 1) / (64 * kDispVecs);
+  const int64_t wpt = ((int64_t)d.K * nch + kWaves - 1) / kWaves;
+  const int64_t want = ((int64_t)d.R * d.S + kXcdsMove - 1) / kXcdsMove * kXcdsMove * wpt;
+  if (d.num_cus > 0) {
+    // a CU budget: the whole grid (padding and token items) within it
+    g.xcd_local = 0;
+    g.item_blocks = 0;
+    g.blocks = capped_grid(c, g.npad_used + want);
+  } else {
+    g.xcd_local = 1;
+    g.item_blocks = (int)want;
+    g.blocks = want + g.npad_used;
+  }
+  return g;
+}
+
+int64_t combine_grid(const Ctx& c, int W) {
+  const int nchunks = (W / 8 + 64 * kCombVecs - 1) / (64 * kCombVecs);
+  return capped_grid(c, ((int64_t)c.d.R * c.d.S * nchunks + kWaves - 1) / kWaves);
+}
+
+int64_t copy_grid(const Ctx& c) {
+  return capped_grid(c, ((int64_t)c.d.R * c.d.NvS + kWaves - 1) / kWaves);
+}
+
+// three workgroups (projections) per 16 KiB column chunk; a CU budget makes them loop over chunks
+int64_t prefetch_grid(const Ctx& c) {
+  return capped_grid(c, 3LL * prefetch_chunks(c.d)) / 3 * 3;
+}
+
+// at most eight workgroups per CU of the device, fewer when there are fewer work items
+int64_t reduce_grad_grid(const Ctx& c) {
+  const Dims& d = c.d;
+  const int64_t max_items = (int64_t)d.R * d.B * 3 * reduce_chunks(d);
+  const int64_t dev = (int64_t)c.num_cu_device * 8;
+  return capped_grid(c, max_items < dev ? max_items : dev);
+}
 
 hipError_t launch_dispatch(const Ctx& c, const moonep_plan_t& p, const uint16_t* x,
                            int W, const float* rw, uint16_t* x_nvs, float* rw_nvs,
@@ -363,21 +422,12 @@ hipError_t launch_dispatch(const Ctx& c, const moonep_plan_t& p, const uint16_t*
   a.dest = p.dest; a.cu = p.cu_seqlens; a.segn = p.seg_tokens; a.act = p.aux + d.aux.act;
   a.ntok = d.R * d.S; a.K = d.K; a.nv = W / 8; a.EB = d.E + d.B; a.L2 = 2 * d.L;
   a.tp = d.tp; a.NvS = (int)d.NvS;
-  a.pad_parts = (d.tp + 4 * kWaves - 1) / (4 * kWaves);
-  a.npad_used = d.R * a.L2 * a.pad_parts;
-  const int nch = (a.nv + 64 * kDispVecs - 1) / (64 * kDispVecs);
-  const int64_t wpt = ((int64_t)a.K * nch + kWaves - 1) / kWaves;
-  const int64_t want = (a.ntok + kXcdsMove - 1) / kXcdsMove * kXcdsMove * wpt;
-  if (d.num_cus > 0) {
-    // a CU budget: the whole grid (padding and token items) within it
-    a.xcd_local = 0;
-    a.item_blocks = 0;
-    dispatch_kernel<<<capped_grid(c, a.npad_used + want), kThreads, 0, s>>>(a);
-  } else {
-    a.xcd_local = 1;
-    a.item_blocks = (int)want;
-    dispatch_kernel<<<(unsigned)(want + a.npad_used), kThreads, 0, s>>>(a);
-  }
+  const DispatchGrid g = dispatch_grid(c, W);
+  a.pad_parts = g.pad_parts;
+  a.npad_used = g.npad_used;
+  a.xcd_local = g.xcd_local;
+  a.item_blocks = g.item_blocks;
+  dispatch_kernel<<<(unsigned)g.blocks, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -387,8 +437,7 @@ hipError_t launch_combine(const Ctx& c, const moonep_plan_t& p, const uint16_t* 
   CombineArgs a;
   a.y = (const u32x4*)y; a.rw_nvs = rw_nvs; a.out = (u32x4*)out; a.rw_sk = rw_sk;
   a.dest = p.dest; a.ntok = d.R * d.S; a.K = d.K; a.nv = W / 8;
-  const int nchunks = (a.nv + 64 * kCombVecs - 1) / (64 * kCombVecs);
-  const int blocks = capped_grid(c, ((int64_t)a.ntok * nchunks + kWaves - 1) / kWaves);
+  const unsigned blocks = (unsigned)combine_grid(c, W);
   if (rw_nvs)
     combine_kernel<true><<<blocks, kThreads, 0, s>>>(a);
   else
@@ -402,7 +451,7 @@ hipError_t launch_copy_rows(const Ctx& c, const moonep_plan_t& p, const uint16_t
   CopyArgs a;
   a.src = (const u32x4*)src; a.dst = (u32x4*)dst; a.cu = p.cu_seqlens;
   a.R = d.R; a.EB = d.E + d.B; a.nv = W / 8; a.NvS = (int)d.NvS;
-  const int blocks = capped_grid(c, ((int64_t)d.R * d.NvS + kWaves - 1) / kWaves);
+  const unsigned blocks = (unsigned)copy_grid(c);
   copy_rows_kernel<<<blocks, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
@@ -422,9 +471,8 @@ hipError_t launch_prefetch(const Ctx& c, const moonep_plan_t& p, const WeightRef
   a.aux_pf = p.aux + d.aux.pf;
   a.aux_pf_n = p.aux + d.aux.pf_n;
   a.row_vecs = (int64_t)d.H * d.Hp / 8;
-  a.nchunks = (int)((a.row_vecs + kThreads * kPrefetchVecs - 1) / (kThreads * kPrefetchVecs));
-  // three workgroups (projections) per chunk; a CU budget makes them loop over chunks
-  const int blocks = capped_grid(c, 3LL * a.nchunks) / 3 * 3;
+  a.nchunks = prefetch_chunks(d);
+  const unsigned blocks = (unsigned)prefetch_grid(c);
   prefetch_kernel<<<blocks, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
@@ -443,11 +491,9 @@ hipError_t launch_reduce_grad(const Ctx& c, const moonep_plan_t& p, float* const
   a.dup_cnt = p.aux + d.aux.dup_cnt;
   a.hold = p.aux + d.aux.hold;
   a.row_vecs = (int64_t)d.H * d.Hp / 4;
-  a.chunk_vecs = kThreads * 16;      // 64 KiB of fp32 per work item
-  a.nchunks = (int)((a.row_vecs + a.chunk_vecs - 1) / a.chunk_vecs);
-  const int64_t max_items = (int64_t)d.R * d.B * 3 * a.nchunks;
-  const int blocks = capped_grid(c, max_items < (int64_t)c.num_cu_device * 8
-                                        ? max_items : (int64_t)c.num_cu_device * 8);
+  a.chunk_vecs = kReduceChunkVecs;
+  a.nchunks = reduce_chunks(d);
+  const unsigned blocks = (unsigned)reduce_grad_grid(c);
   reduce_grad_kernel<<<blocks, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }

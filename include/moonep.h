@@ -121,6 +121,22 @@ int64_t moonep_nvs(const moonep_config_t* cfg);
  * invalid config or index. */
 int64_t moonep_plan_len(const moonep_config_t* cfg, int32_t which);
 
+/* Workgroups that a data-movement call launches for this configuration
+ * (README "API guide", Buffer(..., num_sms, ...): the CU budget caps the
+ * grids of the data-movement kernels; planning and GEMM grids are not
+ * capped).  which: MOONEP_GRID_*.  W: row width in elements for dispatch,
+ * combine and copy (a positive multiple of 8; ignored otherwise).
+ * device_cus: the device's compute units (reduce_grad launches at most 8
+ * workgroups per CU).  Host only: no GPU call is made.  With cfg->num_cus > 0
+ * every result is at most num_cus * 8.  Returns -1 for an invalid config,
+ * which, W or device_cus. */
+enum {
+  MOONEP_GRID_DISPATCH = 0, MOONEP_GRID_COMBINE, MOONEP_GRID_COPY,
+  MOONEP_GRID_PREFETCH, MOONEP_GRID_REDUCE_GRAD
+};
+int64_t moonep_launch_grid(const moonep_config_t* cfg, int32_t which, int32_t W,
+                           int32_t device_cus);
+
 /* Validate cfg (host) and allocate the handle's scratch on the current
  * device (the README's Buffer(...)).  *out is untouched on error. */
 moonep_status_t moonep_create(const moonep_config_t* cfg, moonep_handle_t* out);

@@ -155,3 +155,48 @@ def test_dlpack_wrapper_layout():
     src = torch.arange(16, dtype=torch.float32).to(torch.bfloat16)
     b = _abi.wrap_memory(src.data_ptr(), (4, 4), torch.bfloat16, 1, 0)
     assert b.dtype == torch.bfloat16 and torch.equal(b.reshape(-1), src)
+
+
+GRIDS = [_abi.GRID_DISPATCH, _abi.GRID_COMBINE, _abi.GRID_COPY, _abi.GRID_PREFETCH,
+         _abi.GRID_REDUCE_GRAD]
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_cu_budget_caps_every_data_movement_grid(name):
+    """The launchers size their grids with the same host functions that
+    moonep_launch_grid reports (README "API guide", num_sms): with a CU budget
+    no data-movement launch exceeds num_cus * 8 workgroups, and the budget only
+    ever lowers a grid; without one the grids cover every work item."""
+    w = synth.WORKLOADS[name]
+    for W in (8, 520, w.H, w.Hp):
+        g0 = {k: _abi.launch_grid(_cfg(w), k, W) for k in GRIDS}
+        assert all(v >= 1 for v in g0.values()), g0
+        nvs = _abi.nvs(_cfg(w))
+        # every (token, k, 1024-vector chunk) has a wave, padding items follow
+        assert g0[_abi.GRID_DISPATCH] * 4 >= w.R * w.S * w.K * -(-(W // 8) // 1024)
+        # every (token, 192-vector chunk) of combine, every slot row of copy
+        assert g0[_abi.GRID_COMBINE] * 4 >= w.R * w.S * -(-(W // 8) // 192)
+        assert g0[_abi.GRID_COPY] * 4 >= w.R * nvs
+        assert g0[_abi.GRID_PREFETCH] % 3 == 0
+        assert g0[_abi.GRID_REDUCE_GRAD] <= 256 * 8
+        for num_cus in (1, 3, 32, 256):
+            cap = num_cus * 8
+            for k in GRIDS:
+                g = _abi.launch_grid(_cfg(w, num_cus=num_cus), k, W)
+                assert 1 <= g <= cap, (k, num_cus, g)
+                want = min(g0[k], cap)
+                if k == _abi.GRID_PREFETCH:
+                    want = min(g0[k], cap // 3 * 3)
+                assert g == want, (k, num_cus, g, g0[k])
+
+
+def test_launch_grid_rejects_bad_arguments():
+    w = synth.WORKLOADS["tiny_r4_s64_k2_e8"]
+    c = _cfg(w)
+    assert _abi.launch_grid(c, 99, 8) == -1
+    for k in (_abi.GRID_DISPATCH, _abi.GRID_COMBINE, _abi.GRID_COPY):
+        assert _abi.launch_grid(c, k, 0) == -1
+        assert _abi.launch_grid(c, k, 12) == -1
+    assert _abi.launch_grid(c, _abi.GRID_PREFETCH, 0) >= 3
+    assert _abi.launch_grid(c, _abi.GRID_REDUCE_GRAD, 0, device_cus=0) == -1
+    assert _abi.launch_grid(_cfg(w, K=0), _abi.GRID_DISPATCH, 8) == -1
